@@ -1,0 +1,65 @@
+"""Host logic of the seeded workloads: shapes, reproducibility, tables and
+deltas (no arithmetic of the method lives there)."""
+import numpy as np
+
+from quantization_rope_reuse_amd import workloads as W
+
+
+def test_shapes_and_byte_sizes():
+    assert W.TINY.n_blocks == 4 and W.GQA_REORDER.n_blocks == 84
+    assert W.QWEN3_8B.n_blocks == 512 and W.LLAMA3_70B.n_blocks == 1024
+    assert W.INT4_L3.n_blocks == 256
+    # fp16 Qwen3-8B-shaped cache is 4.5 GiB; bf16 Llama-3-70B-shaped ~21.5 GB
+    assert W.QWEN3_8B.n_vectors * 2 * 128 * 2 == int(4.5 * 2 ** 30)
+    assert W.LLAMA3_70B.n_vectors * 2 * 128 * 2 == 21474836480
+
+
+def test_reorder_plan():
+    old, dm = W.reorder_plan(W.GQA_REORDER)
+    vals, counts = np.unique(dm, return_counts=True)
+    assert dict(zip(vals.tolist(), counts.tolist())) == {-512: 32, 0: 20, 512: 32}
+    assert sorted(old.tolist()) == list(range(84))
+    assert dm[:16].tolist() == [0] * 16 and dm[-4:].tolist() == [0] * 4
+    assert old[16] == (256 + 512) // 16 and old[48] == 256 // 16
+
+
+def test_tables_are_permutations_and_deltas_in_range():
+    for w in W.ALL:
+        for t in (W.put_table(w), W.fetch_table(w)):
+            assert sorted(t.tolist()) == list(range(w.n_blocks))
+        d = W.delta_m(w)
+        assert d.shape == (w.n_blocks,) and d.dtype == np.int32
+        if w.delta_kind == "uniform":
+            assert d.min() >= -w.delta_value and d.max() <= w.delta_value
+            assert d.min() < 0 < d.max()
+    assert np.all(W.delta_m(W.LLAMA3_70B) == 8192)
+    assert np.all(W.delta_m(W.TINY) == 7168)
+
+
+def test_host_values_reproducible_and_outliers():
+    w = W.INT4_L3
+    a = W.host_layer_values(w, 3, 0)
+    b = W.host_layer_values(w, 3, 0)
+    assert np.array_equal(a, b)
+    assert not np.array_equal(a, W.host_layer_values(w, 3, 1))
+    ch = W.outlier_channels(w, 3)
+    assert ch.size == 10
+    flat = a.reshape(w.n_tokens, -1)
+    big = np.abs(flat[:, ch]).mean()
+    rest = np.abs(np.delete(flat, ch, axis=1)).mean()
+    assert 15 < big / rest < 25
+
+
+def test_tiny_values():
+    k, v = W.tiny_pre_rope_kv()
+    g = np.random.default_rng(0)
+    assert np.array_equal(k, g.standard_normal((64, 8, 128)).astype(np.float32))
+    assert W.tiny_positions()[0] == 1024 and W.tiny_positions()[-1] == 1087
+
+
+def test_pages_from_tokens():
+    w = W.TINY
+    x = np.arange(64 * 8 * 128, dtype=np.float32).reshape(64, 8, 128)
+    t = np.array([2, 0, 3, 1])
+    p = W.pages_from_tokens(x, w, t)
+    assert np.array_equal(p[2], x[0:16]) and np.array_equal(p[1], x[48:64])

@@ -1,0 +1,176 @@
+/*
+ * hkv.h - C ABI of libhkv, a KV-cache block codec for AMD MI355X (gfx950).
+ *
+ * libhkv moves cached key/value blocks of a transformer into and out of a
+ * compressed record form and re-uses them at a new token position:
+ *
+ *   put    quantize post-RoPE K and V head vectors of 128 elements to FP8
+ *          E4M3 or to INT4, one fp16 scale per vector (hkv_quant_fp8,
+ *          hkv_quant_int4);
+ *   check  CRC-32 of each record (hkv_crc32_blocks);
+ *   fetch  dequantize, rotate every key pair by the block's position delta
+ *          dm = m_new - m_old, leave values unrotated, and scatter into a
+ *          paged KV buffer through a block table
+ *          (hkv_fetch_dequant_rope_shift).
+ *
+ * The operations follow two web pages:
+ *   "HyperCache – Distributed KV-cache quantization and relative RoPE reuse"
+ *   (the HyperCache post): Core Design, relative-RoPE paragraph with the SO(2)
+ *   identity R(m_new th_i) = R(dm th_i) R(m_old th_i); the compression
+ *   paragraph and the Part B benchmark printout (FP8 E4M3 wire records,
+ *   INT4 grouped disk records with CRC32).
+ *   "Модуль 13: KV-хэндофф: передача кеша между моделями и узлами" of the
+ *   LLM Inference Systems course (the KV-handoff module): the module13.py
+ *   listing's rope_cache / apply_rope, which fix th_i = 1 / base^(2i/d) and the rotation
+ *   (a, b) -> (a cos - b sin, a sin + b cos).
+ *
+ * Conventions for every call
+ * --------------------------
+ * - All array pointers are DEVICE pointers owned by the caller; the structs
+ *   themselves are read from host memory during the call only.
+ * - Calls are asynchronous on `stream` (0 = the default stream), allocate
+ *   no memory, keep no state between calls and may be called from several
+ *   host threads at once.
+ * - Return value: HKV_OK (0) or a negative hkv_status.  Argument errors are
+ *   detected on the host before anything is launched; nothing throws across
+ *   the ABI.  A launch failure is reported as HKV_ERR_HIP.
+ * - head_dim must be 128 (the group of one scale).
+ * - Zero layers or zero blocks is a valid empty call that launches nothing.
+ * - Block tables are int32 [n_blocks]: logical block -> page.  A negative
+ *   entry means "skip this block"; an entry >= num_pages is skipped as well
+ *   (it is never dereferenced).  The tables given to one call must not map
+ *   two blocks to the same page (the writes would race).
+ */
+#ifndef HKV_H
+#define HKV_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  HKV_OK = 0,
+  HKV_ERR_INVALID_ARG = -1,  /* null pointer, bad size, misalignment, bad enum */
+  HKV_ERR_UNSUPPORTED = -2,  /* a well-formed request this build does not do  */
+  HKV_ERR_HIP = -3           /* the HIP runtime reported a launch error        */
+} hkv_status;
+
+typedef enum { HKV_F32 = 0, HKV_F16 = 1, HKV_BF16 = 2 } hkv_dtype;
+typedef enum { HKV_FP8_E4M3 = 0, HKV_INT4 = 1 } hkv_format;
+typedef enum { HKV_ROPE_INTERLEAVED = 0, HKV_ROPE_HALF_SPLIT = 1 } hkv_rope_pairs;
+
+#define HKV_HEAD_DIM 128
+
+/* Geometry shared by all calls.  A "vector" is one (layer, K|V, token, head)
+ * row of head_dim elements. */
+typedef struct {
+  int32_t n_layers;      /* >= 0 */
+  int32_t n_blocks;      /* >= 0, logical blocks per layer */
+  int32_t block_tokens;  /* >= 1, tokens per block (= tokens per page) */
+  int32_t n_kv_heads;    /* >= 1 */
+  int32_t head_dim;      /* must be 128 */
+} hkv_shape;
+
+/* An engine's paged KV buffer: separate K and V arrays of one dtype.
+ * Element (layer l, page p, token t, head h, dim j) of K is at
+ *   k + l*layer_stride + p*page_stride + t*token_stride + h*head_stride + j
+ * (strides in ELEMENTS, non-negative; the head_dim elements of a vector are
+ * contiguous).  k, v and every stride times the element size must be
+ * multiples of 16 bytes. */
+typedef struct {
+  void* k;
+  void* v;
+  int64_t layer_stride;
+  int64_t page_stride;
+  int64_t token_stride;
+  int64_t head_stride;
+  int32_t num_pages;     /* pages per layer; table entries >= this are skipped */
+} hkv_pages;
+
+/* Compressed records, one per (layer, logical block), record (l, b) at
+ *   base + l*layer_stride_bytes + b*block_stride_bytes.
+ * Record layout (N = block_tokens * n_kv_heads vectors, C = 128 code bytes
+ * for FP8 or 64 for INT4):
+ *   [K codes N*C][V codes N*C][K scales N*2][V scales N*2]
+ * codes ordered token-major, then head, then element; scales are IEEE fp16,
+ * little endian, in the same vector order.  INT4 packs element 2k in the
+ * low nibble and 2k+1 in the high nibble of byte k, two's complement.
+ * base and both strides must be multiples of 16 bytes and the block stride
+ * at least hkv_record_bytes(). */
+typedef struct {
+  void* base;
+  int64_t layer_stride_bytes;
+  int64_t block_stride_bytes;
+} hkv_records;
+
+/* Put, FP8 (HyperCache post: compression paragraph; Part B, the FP8 E4M3
+ * wire line, 1.97x against fp16).
+ * For every vector x of logical block b (read from page block_table[b] of
+ * `src`, dtype src_dtype):
+ *   amax = max_j |x_j|                       (exact, fp32)
+ *   s    = fp16_RNE(amax / 448)              (IEEE fp32 division)
+ *          with s = 2^-24 if that rounds to 0 while amax > 0, and
+ *          s = 65504 if it exceeds the fp16 range; s = 0 if amax = 0
+ *   c_j  = E4M3FN_RNE(x_j / s), saturating at +-448, sign of zero kept
+ *          (x_j itself, a signed zero, when s = 0)
+ * and writes codes and s to record (l, b) of `dst`.  Records of skipped
+ * blocks are not written. */
+int hkv_quant_fp8(const hkv_shape* shape, const hkv_pages* src, int32_t src_dtype,
+                  const int32_t* block_table, const hkv_records* dst,
+                  hipStream_t stream);
+
+/* Put, INT4 grouped symmetric (HyperCache post: Part B, the grouped INT4
+ * L3-disk line, 3.88x against fp16).  As hkv_quant_fp8 with
+ *   s   = fp16_RNE(amax / 7) (same edge cases),
+ *   q_j = clamp(round_half_even(x_j / s), -7, 7). */
+int hkv_quant_int4(const hkv_shape* shape, const hkv_pages* src, int32_t src_dtype,
+                   const int32_t* block_table, const hkv_records* dst,
+                   hipStream_t stream);
+
+/* Fetch (HyperCache post: Core Design, relative-RoPE paragraph; Part B, the
+ * socket-fetch line with RoPE applied on the fly).
+ * For every layer l and logical block b with 0 <= block_table[b] < num_pages:
+ *   y = code * s                                      (exact in fp32)
+ *   V: y unchanged.
+ *   K: each pair i = 0..63 - elements (2i, 2i+1) for HKV_ROPE_INTERLEAVED,
+ *      (i, i+64) for HKV_ROPE_HALF_SPLIT - is rotated by
+ *      phi = delta_m[b] * th_i, th_i = 1 / rope_base^(2i/128):
+ *        (a, b) -> (a cos phi - b sin phi, a sin phi + b cos phi),
+ *      with phi, cos and sin evaluated in double precision (full range
+ *      reduction) and rounded to fp32 once per (block, i); a block with
+ *      delta_m[b] = 0 is passed through unrotated.
+ *   The result is rounded to nearest even to dst_dtype and stored at page
+ *   block_table[b] of `dst`, token t, head h.
+ * delta_m: int32 [n_blocks] device array, any sign.
+ * rope_base: finite and > 0. */
+int hkv_fetch_dequant_rope_shift(const hkv_shape* shape, int32_t fmt,
+                                 const hkv_records* src, const int32_t* block_table,
+                                 const int32_t* delta_m, double rope_base,
+                                 int32_t pairs, const hkv_pages* dst,
+                                 int32_t dst_dtype, hipStream_t stream);
+
+/* CRC-32 of every record (HyperCache post: Part B, the L3-disk line with its
+ * per-file CRC32, and the tamper-detection tests of its test-suite section).  The common zlib variant:
+ * reflected polynomial 0xEDB88320, initial value and final xor 0xFFFFFFFF,
+ * over the hkv_record_bytes() bytes of each record.
+ * crc_out: uint32 [n_layers * n_blocks] device array, layer-major. */
+int hkv_crc32_blocks(const hkv_shape* shape, int32_t fmt, const hkv_records* src,
+                     uint32_t* crc_out, hipStream_t stream);
+
+/* Host-only helpers. */
+
+/* Bytes of one record: 2*N*C + 4*N (see hkv_records); -1 on bad arguments. */
+int64_t hkv_record_bytes(int32_t fmt, int32_t block_tokens, int32_t n_kv_heads,
+                         int32_t head_dim);
+
+/* Static, NUL-terminated description of a status code. */
+const char* hkv_status_string(int32_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HKV_H */

@@ -314,7 +314,9 @@ def put(k_pages, v_pages, block_table, fmt):
 
     k_pages, v_pages: [L, P, T_b, H, 128] source values (any float dtype; they
     are taken at their exact fp32 value).  block_table: [n_blocks] int, logical
-    block -> page, negative entries skipped.
+    block -> page; entries that are negative or not below the page count are
+    skipped (reading: a negative entry marks a block to skip, and an entry
+    past the buffer is never dereferenced).
     Returns (records uint8 [L, n_blocks, rec_bytes], written bool [n_blocks]);
     records of skipped blocks are all zero.
     """
@@ -324,7 +326,7 @@ def put(k_pages, v_pages, block_table, fmt):
     nb = table.shape[0]
     rb = record_bytes(fmt, T_b, H, d)
     out = np.zeros((L, nb, rb), dtype=np.uint8)
-    live = table >= 0
+    live = (table >= 0) & (table < P)
     pages = table[live]
     quant = quant_fp8_vectors if fmt == FMT_FP8 else quant_int4_vectors
     kx = np.asarray(k_pages)[:, pages].astype(np.float32)
@@ -458,10 +460,11 @@ def fetch_exact(records, fmt, block_tokens, n_kv_heads, delta_m, base, pairs):
 def fetch(records, fmt, block_tokens, n_kv_heads, block_table, delta_m, base,
           pairs, k_pages, v_pages, out_dtype):
     """Fetch into page arrays k_pages, v_pages [L, P, T_b, H, 128] (float64
-    carriers of the page dtype, modified in place).  Blocks with a negative
-    table entry are skipped and their pages keep their contents."""
+    carriers of the page dtype, modified in place).  Blocks whose table entry
+    is negative or not below the page count are skipped; pages that no block
+    names keep their contents."""
     table = np.asarray(block_table, dtype=np.int64)
-    live = table >= 0
+    live = (table >= 0) & (table < k_pages.shape[1])
     kr, vd = fetch_exact(records[:, live], fmt, block_tokens, n_kv_heads,
                          np.asarray(delta_m)[live], base, pairs)
     k_pages[:, table[live]] = round_output(kr, out_dtype)

@@ -1,0 +1,178 @@
+// libhkv C ABI: argument validation and dispatch to the kernel launchers.
+// Every check runs on the host before any HIP call, so argument errors are
+// reported without touching a device.
+#include "hkv.h"
+
+#include <math.h>
+#include <stdint.h>
+
+#include "hkv_device.h"
+#include "hkv_launch.h"
+
+namespace {
+
+using hkv::Geometry;
+using hkv::PageView;
+using hkv::RecordView;
+
+int elem_size(int32_t dtype) {
+  switch (dtype) {
+    case HKV_F32: return 4;
+    case HKV_F16: return 2;
+    case HKV_BF16: return 2;
+    default: return 0;
+  }
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int64_t code_bytes(int32_t fmt) { return fmt == HKV_FP8_E4M3 ? 128 : 64; }
+
+bool valid_format(int32_t fmt) { return fmt == HKV_FP8_E4M3 || fmt == HKV_INT4; }
+
+// Shape checks common to every call; fills the launch geometry.
+int check_shape(const hkv_shape* s, Geometry* g) {
+  if (!s) return HKV_ERR_INVALID_ARG;
+  if (s->n_layers < 0 || s->n_blocks < 0 || s->block_tokens < 1 || s->n_kv_heads < 1)
+    return HKV_ERR_INVALID_ARG;
+  if (s->head_dim != HKV_HEAD_DIM) return HKV_ERR_INVALID_ARG;
+  if (s->n_layers > 65535) return HKV_ERR_UNSUPPORTED;            // grid.y limit
+  const int64_t vecs = static_cast<int64_t>(s->block_tokens) * s->n_kv_heads;
+  if (vecs > (1 << 24)) return HKV_ERR_UNSUPPORTED;
+  if (static_cast<int64_t>(s->n_layers) * s->n_blocks > INT32_MAX) return HKV_ERR_UNSUPPORTED;
+  g->n_layers = s->n_layers;
+  g->n_blocks = s->n_blocks;
+  g->block_tokens = s->block_tokens;
+  g->n_heads = s->n_kv_heads;
+  g->vecs = static_cast<int32_t>(vecs);
+  // Up to 256 vectors (8 passes of a 4-wave workgroup) per workgroup.
+  const int32_t per_wg = 256;
+  g->chunks = static_cast<int32_t>((vecs + per_wg - 1) / per_wg);
+  const int64_t even = (vecs + g->chunks - 1) / g->chunks;          // balance the chunks
+  g->vecs_per_chunk = static_cast<int32_t>((even + hkv::kVecsPerPass - 1) /
+                                           hkv::kVecsPerPass * hkv::kVecsPerPass);
+  if (static_cast<int64_t>(s->n_blocks) * 2 * g->chunks > INT32_MAX) return HKV_ERR_UNSUPPORTED;
+  return HKV_OK;
+}
+
+int check_pages(const hkv_pages* p, int32_t dtype, PageView* v) {
+  if (!p) return HKV_ERR_INVALID_ARG;
+  const int es = elem_size(dtype);
+  if (es == 0) return HKV_ERR_INVALID_ARG;
+  if (!p->k || !p->v || !aligned16(p->k) || !aligned16(p->v)) return HKV_ERR_INVALID_ARG;
+  if (p->num_pages < 0) return HKV_ERR_INVALID_ARG;
+  const int64_t st[4] = {p->layer_stride, p->page_stride, p->token_stride, p->head_stride};
+  for (int64_t x : st) {
+    if (x < 0 || x > (INT64_MAX / 8)) return HKV_ERR_INVALID_ARG;
+    if ((x * es) % 16 != 0) return HKV_ERR_INVALID_ARG;
+  }
+  v->k = static_cast<char*>(p->k);
+  v->v = static_cast<char*>(p->v);
+  v->layer = p->layer_stride * es;
+  v->page = p->page_stride * es;
+  v->token = p->token_stride * es;
+  v->head = p->head_stride * es;
+  v->num_pages = p->num_pages;
+  return HKV_OK;
+}
+
+int check_records(const hkv_records* r, int32_t fmt, const hkv_shape* s, RecordView* v) {
+  if (!r || !r->base || !aligned16(r->base)) return HKV_ERR_INVALID_ARG;
+  if (r->layer_stride_bytes < 0 || r->block_stride_bytes < 0) return HKV_ERR_INVALID_ARG;
+  if (r->layer_stride_bytes % 16 != 0 || r->block_stride_bytes % 16 != 0)
+    return HKV_ERR_INVALID_ARG;
+  const int64_t rb = hkv_record_bytes(fmt, s->block_tokens, s->n_kv_heads, s->head_dim);
+  if (rb < 0) return HKV_ERR_INVALID_ARG;
+  if (s->n_blocks > 1 && r->block_stride_bytes < rb) return HKV_ERR_INVALID_ARG;
+  if (s->n_layers > 1 && r->layer_stride_bytes < rb) return HKV_ERR_INVALID_ARG;
+  v->base = static_cast<uint8_t*>(r->base);
+  v->layer = r->layer_stride_bytes;
+  v->block = r->block_stride_bytes;
+  return HKV_OK;
+}
+
+int to_status(hipError_t e) { return e == hipSuccess ? HKV_OK : HKV_ERR_HIP; }
+
+int quant_common(int32_t fmt, const hkv_shape* shape, const hkv_pages* src, int32_t src_dtype,
+                 const int32_t* block_table, const hkv_records* dst, hipStream_t stream) {
+  Geometry g;
+  PageView pv;
+  RecordView rv;
+  int st;
+  if ((st = check_shape(shape, &g)) != HKV_OK) return st;
+  if ((st = check_pages(src, src_dtype, &pv)) != HKV_OK) return st;
+  if ((st = check_records(dst, fmt, shape, &rv)) != HKV_OK) return st;
+  if (!block_table && g.n_blocks > 0) return HKV_ERR_INVALID_ARG;
+  if (g.n_layers == 0 || g.n_blocks == 0) return HKV_OK;
+  return to_status(hkv::launch_quant(fmt, src_dtype, g, pv, block_table, rv, stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t hkv_record_bytes(int32_t fmt, int32_t block_tokens, int32_t n_kv_heads,
+                         int32_t head_dim) {
+  if (!valid_format(fmt) || block_tokens < 1 || n_kv_heads < 1 || head_dim != HKV_HEAD_DIM)
+    return -1;
+  const int64_t n = static_cast<int64_t>(block_tokens) * n_kv_heads;
+  return 2 * n * code_bytes(fmt) + 4 * n;
+}
+
+const char* hkv_status_string(int32_t status) {
+  switch (status) {
+    case HKV_OK: return "ok";
+    case HKV_ERR_INVALID_ARG: return "invalid argument";
+    case HKV_ERR_UNSUPPORTED: return "unsupported request";
+    case HKV_ERR_HIP: return "HIP launch error";
+    default: return "unknown status";
+  }
+}
+
+int hkv_quant_fp8(const hkv_shape* shape, const hkv_pages* src, int32_t src_dtype,
+                  const int32_t* block_table, const hkv_records* dst, hipStream_t stream) {
+  return quant_common(HKV_FP8_E4M3, shape, src, src_dtype, block_table, dst, stream);
+}
+
+int hkv_quant_int4(const hkv_shape* shape, const hkv_pages* src, int32_t src_dtype,
+                   const int32_t* block_table, const hkv_records* dst, hipStream_t stream) {
+  return quant_common(HKV_INT4, shape, src, src_dtype, block_table, dst, stream);
+}
+
+int hkv_fetch_dequant_rope_shift(const hkv_shape* shape, int32_t fmt, const hkv_records* src,
+                                 const int32_t* block_table, const int32_t* delta_m,
+                                 double rope_base, int32_t pairs, const hkv_pages* dst,
+                                 int32_t dst_dtype, hipStream_t stream) {
+  Geometry g;
+  PageView pv;
+  RecordView rv;
+  int st;
+  if (!valid_format(fmt)) return HKV_ERR_INVALID_ARG;
+  if ((st = check_shape(shape, &g)) != HKV_OK) return st;
+  if ((st = check_records(src, fmt, shape, &rv)) != HKV_OK) return st;
+  if ((st = check_pages(dst, dst_dtype, &pv)) != HKV_OK) return st;
+  if (pairs != HKV_ROPE_INTERLEAVED && pairs != HKV_ROPE_HALF_SPLIT) return HKV_ERR_INVALID_ARG;
+  if (!(rope_base > 0.0) || !isfinite(rope_base)) return HKV_ERR_INVALID_ARG;
+  if ((!block_table || !delta_m) && g.n_blocks > 0) return HKV_ERR_INVALID_ARG;
+  if (g.n_layers == 0 || g.n_blocks == 0) return HKV_OK;
+  return to_status(hkv::launch_fetch(fmt, dst_dtype, pairs, g, rv, block_table, delta_m,
+                                     rope_base, pv, stream));
+}
+
+int hkv_crc32_blocks(const hkv_shape* shape, int32_t fmt, const hkv_records* src,
+                     uint32_t* crc_out, hipStream_t stream) {
+  Geometry g;
+  RecordView rv;
+  int st;
+  if (!valid_format(fmt)) return HKV_ERR_INVALID_ARG;
+  if ((st = check_shape(shape, &g)) != HKV_OK) return st;
+  if ((st = check_records(src, fmt, shape, &rv)) != HKV_OK) return st;
+  if (!crc_out && g.n_layers > 0 && g.n_blocks > 0) return HKV_ERR_INVALID_ARG;
+  if (g.n_layers == 0 || g.n_blocks == 0) return HKV_OK;
+  const int64_t rb = hkv_record_bytes(fmt, shape->block_tokens, shape->n_kv_heads,
+                                      shape->head_dim);
+  if (rb > (int64_t{1} << 30)) return HKV_ERR_UNSUPPORTED;
+  return to_status(hkv::launch_crc32(g, rb, rv, crc_out, stream));
+}
+
+}  // extern "C"

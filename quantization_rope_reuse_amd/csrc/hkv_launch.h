@@ -1,0 +1,44 @@
+// Internal launch interface between the validated C ABI (api.hip) and the
+// kernel sources.  All strides here are in BYTES; the ABI layer converts the
+// element strides of hkv_pages.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace hkv {
+
+// Geometry of one call, after validation.
+struct Geometry {
+  int32_t n_layers;
+  int32_t n_blocks;
+  int32_t block_tokens;
+  int32_t n_heads;
+  int32_t vecs;            // block_tokens * n_heads vectors per (block, K|V)
+  int32_t chunks;          // workgroups per (layer, block, K|V)
+  int32_t vecs_per_chunk;  // multiple of kVecsPerPass (32)
+};
+
+struct PageView {          // byte addressing of a paged buffer
+  char* k;
+  char* v;
+  int64_t layer, page, token, head;
+  int32_t num_pages;
+};
+
+struct RecordView {
+  uint8_t* base;
+  int64_t layer, block;
+};
+
+hipError_t launch_quant(int fmt, int src_dtype, const Geometry& g, const PageView& src,
+                        const int32_t* table, const RecordView& dst, hipStream_t stream);
+
+hipError_t launch_fetch(int fmt, int dst_dtype, int pairs, const Geometry& g,
+                        const RecordView& src, const int32_t* table, const int32_t* delta_m,
+                        double rope_base, const PageView& dst, hipStream_t stream);
+
+hipError_t launch_crc32(const Geometry& g, int64_t record_bytes, const RecordView& src,
+                        uint32_t* out, hipStream_t stream);
+
+}  // namespace hkv

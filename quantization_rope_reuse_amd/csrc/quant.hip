@@ -1,0 +1,163 @@
+// Put: quantize the K and V head vectors of blocks gathered from a paged
+// buffer into compressed records, FP8 E4M3 or INT4, one fp16 scale per
+// 128-element vector.
+//
+// Follows the HyperCache post ("HyperCache – Distributed KV-cache
+// quantization and relative RoPE reuse"), Core Design, compression
+// paragraph, and its Part B printout (FP8 E4M3 wire records at 1.97x and
+// grouped INT4 disk records at 3.88x against fp16).  Per vector:
+//   amax = max |x_j|; s = fp16_RNE(amax / qmax) (qmax 448 for E4M3, 7 for
+//   INT4; IEEE fp32 division); code_j = round(x_j / s) to E4M3 (saturating
+//   at +-448) or to an integer clamped to [-7, 7].
+//
+// Work decomposition matches the fetch kernel: one workgroup per (layer,
+// block, K|V, chunk), 8 lanes per vector; the vector's amax is reduced over
+// its 8 lanes with cross-lane max.
+#include "hkv_device.h"
+#include "hkv_launch.h"
+
+namespace hkv {
+namespace {
+
+struct QuantParams {
+  const char* k_src;
+  const char* v_src;
+  int64_t s_layer, s_page, s_token, s_head;
+  int32_t num_pages;
+  const int32_t* table;
+  uint8_t* rec;
+  int64_t rec_layer, rec_block;
+  int32_t n_heads;
+  int32_t vecs;
+  int32_t chunks;
+  int32_t vecs_per_chunk;
+};
+
+// fp16 bits of the scale for a vector with max magnitude amax (fp32).
+// Edge cases: amax == 0 -> 0; a positive amax whose scale underflows fp16 ->
+// smallest subnormal (0x0001); a scale beyond the fp16 range -> 65504.
+template <int QMAX>
+__device__ __forceinline__ uint32_t scale_bits(float amax) {
+  const float s32 = amax / static_cast<float>(QMAX);   // IEEE division
+  uint32_t h = f32_to_f16_bits(s32);
+  if (h == 0x7C00u) h = 0x7BFFu;
+  if (h == 0u && amax > 0.0f) h = 0x0001u;
+  return h;
+}
+
+template <int FMT, int SDT>
+__global__ __launch_bounds__(kThreads) void quant_kernel(QuantParams p) {
+  const int layer = blockIdx.y;
+  const int chunk = blockIdx.x % p.chunks;
+  const int bk = blockIdx.x / p.chunks;
+  const int kv = bk & 1;
+  const int blk = bk >> 1;
+  const int page = p.table[blk];
+  if (page < 0 || page >= p.num_pages) return;
+
+  constexpr int CB = FMT == kFP8 ? kHeadDim : kHeadDim / 2;
+  constexpr int ES = ElemSize<SDT>::value;
+  const char* src = (kv ? p.v_src : p.k_src) + layer * p.s_layer + page * p.s_page;
+  uint8_t* rec = p.rec + layer * p.rec_layer + blk * p.rec_block;
+  uint8_t* codes = rec + static_cast<int64_t>(kv) * p.vecs * CB;
+  uint16_t* scales = reinterpret_cast<uint16_t*>(rec + 2LL * p.vecs * CB + 2LL * kv * p.vecs);
+
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int sub = lane & (kLanesPerVec - 1);
+  const int vsub = lane / kLanesPerVec;
+  const int v_begin = chunk * p.vecs_per_chunk;
+  const int v_end = min(v_begin + p.vecs_per_chunk, p.vecs);
+
+  for (int v = v_begin + wave * kVecsPerWave + vsub; v < v_end; v += kVecsPerPass) {
+    const int t = v / p.n_heads;
+    const int h = v - t * p.n_heads;
+    const char* x_ptr = src + t * p.s_token + h * p.s_head + 8 * sub * ES;
+    float a[8], b[8];
+    load8<SDT>(x_ptr, a);
+    load8<SDT>(x_ptr + 64 * ES, b);
+
+    float m = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) m = fmaxf(m, fmaxf(fabsf(a[j]), fabsf(b[j])));
+    const float amax = max_over_vector_lanes(m);
+
+    constexpr int QMAX = FMT == kFP8 ? 448 : 7;
+    const uint32_t sbits = scale_bits<QMAX>(amax);
+    const float s = f16_bits_to_f32(sbits);
+    const bool zero_scale = sbits == 0u;
+
+    float qa[8], qb[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      qa[j] = zero_scale ? a[j] : a[j] / s;            // IEEE division
+      qb[j] = zero_scale ? b[j] : b[j] / s;
+    }
+
+    uint8_t* c_ptr = codes + static_cast<int64_t>(v) * CB;
+    if constexpr (FMT == kFP8) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        qa[j] = fminf(fmaxf(qa[j], -448.0f), 448.0f);
+        qb[j] = fminf(fmaxf(qb[j], -448.0f), 448.0f);
+      }
+      *reinterpret_cast<u32x2*>(c_ptr + 8 * sub) = f32x8_to_fp8(qa);
+      *reinterpret_cast<u32x2*>(c_ptr + 64 + 8 * sub) = f32x8_to_fp8(qb);
+    } else {
+      uint32_t wa = 0, wb = 0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int ia = static_cast<int>(fminf(fmaxf(rintf(qa[j]), -7.0f), 7.0f));
+        const int ib = static_cast<int>(fminf(fmaxf(rintf(qb[j]), -7.0f), 7.0f));
+        wa |= (static_cast<uint32_t>(ia) & 0xFu) << (4 * j);
+        wb |= (static_cast<uint32_t>(ib) & 0xFu) << (4 * j);
+      }
+      *reinterpret_cast<uint32_t*>(c_ptr + 4 * sub) = wa;
+      *reinterpret_cast<uint32_t*>(c_ptr + 32 + 4 * sub) = wb;
+    }
+    if (sub == 0) scales[v] = static_cast<uint16_t>(sbits);
+  }
+}
+
+template <int FMT, int SDT>
+hipError_t launch_t(const QuantParams& p, const Geometry& g, hipStream_t stream) {
+  dim3 grid(static_cast<unsigned>(g.n_blocks) * 2u * static_cast<unsigned>(g.chunks),
+            static_cast<unsigned>(g.n_layers));
+  hipLaunchKernelGGL((quant_kernel<FMT, SDT>), grid, dim3(kThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
+template <int FMT>
+hipError_t launch_dtype(int sdt, const QuantParams& p, const Geometry& g, hipStream_t s) {
+  switch (sdt) {
+    case kF32: return launch_t<FMT, kF32>(p, g, s);
+    case kF16: return launch_t<FMT, kF16>(p, g, s);
+    default: return launch_t<FMT, kBF16>(p, g, s);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_quant(int fmt, int src_dtype, const Geometry& g, const PageView& src,
+                        const int32_t* table, const RecordView& dst, hipStream_t stream) {
+  QuantParams p;
+  p.k_src = src.k;
+  p.v_src = src.v;
+  p.s_layer = src.layer;
+  p.s_page = src.page;
+  p.s_token = src.token;
+  p.s_head = src.head;
+  p.num_pages = src.num_pages;
+  p.table = table;
+  p.rec = dst.base;
+  p.rec_layer = dst.layer;
+  p.rec_block = dst.block;
+  p.n_heads = g.n_heads;
+  p.vecs = g.vecs;
+  p.chunks = g.chunks;
+  p.vecs_per_chunk = g.vecs_per_chunk;
+  return fmt == kFP8 ? launch_dtype<kFP8>(src_dtype, p, g, stream)
+                     : launch_dtype<kINT4>(src_dtype, p, g, stream);
+}
+
+}  // namespace hkv

@@ -1,0 +1,226 @@
+"""Thin ctypes binding of libhkv (include/hkv.h).
+
+Argument marshalling only: every step of put, CRC and fetch runs in the HIP
+kernels of libhkv.so.  torch is used for device memory and streams: tensors
+supply device pointers and strides, and calls are enqueued on the caller's
+current torch stream unless another is given.
+
+There is no fallback: if libhkv.so is missing or cannot be loaded, importing
+the library raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import torch  # load torch's HIP runtime first so libhkv binds to the same one
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libhkv.so")
+HEADER = os.path.join(os.path.dirname(HERE), "include", "hkv.h")
+
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_HIP = 0, -1, -2, -3
+F32, F16, BF16 = 0, 1, 2
+FP8_E4M3, INT4 = 0, 1
+ROPE_INTERLEAVED, ROPE_HALF_SPLIT = 0, 1
+HEAD_DIM = 128
+
+FORMATS = {"fp8": FP8_E4M3, "int4": INT4, FP8_E4M3: FP8_E4M3, INT4: INT4}
+PAIRS = {"interleaved": ROPE_INTERLEAVED, "half_split": ROPE_HALF_SPLIT,
+         ROPE_INTERLEAVED: ROPE_INTERLEAVED, ROPE_HALF_SPLIT: ROPE_HALF_SPLIT}
+TORCH_DTYPES = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16}
+
+
+class HkvError(RuntimeError):
+    def __init__(self, call, status):
+        self.status = status
+        super().__init__(f"{call} failed: {status_string(status)} ({status})")
+
+
+class Shape(ctypes.Structure):
+    _fields_ = [("n_layers", ctypes.c_int32), ("n_blocks", ctypes.c_int32),
+                ("block_tokens", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32)]
+
+
+class Pages(ctypes.Structure):
+    _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+                ("layer_stride", ctypes.c_int64), ("page_stride", ctypes.c_int64),
+                ("token_stride", ctypes.c_int64), ("head_stride", ctypes.c_int64),
+                ("num_pages", ctypes.c_int32)]
+
+
+class Records(ctypes.Structure):
+    _fields_ = [("base", ctypes.c_void_p), ("layer_stride_bytes", ctypes.c_int64),
+                ("block_stride_bytes", ctypes.c_int64)]
+
+
+_lib = None
+
+
+def declared_symbols():
+    """Names of the functions include/hkv.h declares."""
+    with open(HEADER) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(hkv_[a-z0-9_]+)\s*\(", text)))
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is not built; run "
+                              "`python -m quantization_rope_reuse_amd.build`")
+        l = ctypes.CDLL(LIB_PATH)
+        P = ctypes.POINTER
+        vp = ctypes.c_void_p
+        l.hkv_quant_fp8.argtypes = [P(Shape), P(Pages), ctypes.c_int32, vp, P(Records), vp]
+        l.hkv_quant_int4.argtypes = [P(Shape), P(Pages), ctypes.c_int32, vp, P(Records), vp]
+        l.hkv_fetch_dequant_rope_shift.argtypes = [
+            P(Shape), ctypes.c_int32, P(Records), vp, vp, ctypes.c_double, ctypes.c_int32,
+            P(Pages), ctypes.c_int32, vp]
+        l.hkv_crc32_blocks.argtypes = [P(Shape), ctypes.c_int32, P(Records), vp, vp]
+        for name in ("hkv_quant_fp8", "hkv_quant_int4", "hkv_fetch_dequant_rope_shift",
+                     "hkv_crc32_blocks"):
+            getattr(l, name).restype = ctypes.c_int
+        l.hkv_record_bytes.argtypes = [ctypes.c_int32] * 4
+        l.hkv_record_bytes.restype = ctypes.c_int64
+        l.hkv_status_string.argtypes = [ctypes.c_int32]
+        l.hkv_status_string.restype = ctypes.c_char_p
+        _lib = l
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().hkv_status_string(int(status)).decode()
+
+
+def record_bytes(fmt, block_tokens: int, n_kv_heads: int, head_dim: int = HEAD_DIM) -> int:
+    return int(lib().hkv_record_bytes(FORMATS[fmt], block_tokens, n_kv_heads, head_dim))
+
+
+# ---------------------------------------------------------------------------
+# Marshalling helpers
+# ---------------------------------------------------------------------------
+
+def _stream(stream, device):
+    if stream is None:
+        return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+    if isinstance(stream, torch.cuda.Stream):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(int(stream))
+
+
+def _as5d(t: torch.Tensor) -> torch.Tensor:
+    """Pages as [L, P, T_b, H, 128]; a 4-D tensor is one layer."""
+    if t.dim() == 4:
+        return t.unsqueeze(0)
+    if t.dim() != 5:
+        raise ValueError("pages must be [L, P, T_b, H, 128] or [P, T_b, H, 128]")
+    return t
+
+
+def _pages(k: torch.Tensor, v: torch.Tensor):
+    k5, v5 = _as5d(k), _as5d(v)
+    if k5.shape != v5.shape or k5.stride() != v5.stride() or k5.dtype != v5.dtype:
+        raise ValueError("K and V pages must share shape, strides and dtype")
+    if k5.shape[-1] != HEAD_DIM or k5.stride(-1) != 1:
+        raise ValueError("the last (head_dim=128) axis of the pages must be contiguous")
+    if k5.dtype not in TORCH_DTYPES:
+        raise ValueError(f"unsupported page dtype {k5.dtype}")
+    s = k5.stride()
+    p = Pages(k5.data_ptr(), v5.data_ptr(), s[0], s[1], s[2], s[3], k5.shape[1])
+    return p, k5.shape, TORCH_DTYPES[k5.dtype]
+
+
+def _records(r: torch.Tensor):
+    """Records as a uint8 tensor [L, n_blocks, >= record_bytes]."""
+    if r.dtype != torch.uint8 or r.dim() != 3 or r.stride(2) != 1:
+        raise ValueError("records must be a uint8 [L, n_blocks, bytes] tensor, last axis contiguous")
+    return Records(r.data_ptr(), r.stride(0), r.stride(1))
+
+
+def _i32(t: torch.Tensor, name: str):
+    if t.dtype != torch.int32 or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous int32 tensor")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _check(call: str, status: int):
+    if status != OK:
+        raise HkvError(call, status)
+
+
+def alloc_records(n_layers: int, n_blocks: int, fmt, block_tokens: int, n_kv_heads: int,
+                  device="cuda"):
+    """A uint8 [L, n_blocks, record_bytes] tensor (block stride rounded up to 16)."""
+    rb = record_bytes(fmt, block_tokens, n_kv_heads)
+    stride = (rb + 15) // 16 * 16
+    buf = torch.empty((n_layers, n_blocks, stride), dtype=torch.uint8, device=device)
+    return buf[:, :, :rb]
+
+
+# ---------------------------------------------------------------------------
+# The four calls
+# ---------------------------------------------------------------------------
+
+def _quant(name, k_pages, v_pages, block_table, records, stream):
+    pages, shp, dt = _pages(k_pages, v_pages)
+    L, _, tb, H, d = shp
+    if records.shape[0] != L or records.shape[1] != block_table.numel():
+        raise ValueError("records must be [L, n_blocks, bytes] matching pages and table")
+    shape = Shape(L, block_table.numel(), tb, H, d)
+    rec = _records(records)
+    st = getattr(lib(), name)(ctypes.byref(shape), ctypes.byref(pages), dt,
+                              _i32(block_table, "block_table"), ctypes.byref(rec),
+                              _stream(stream, k_pages.device))
+    _check(name, st)
+    return records
+
+
+def quant_fp8(k_pages, v_pages, block_table, records, stream=None):
+    """Quantize the blocks k/v_pages[:, block_table[b]] into records[:, b] (FP8)."""
+    return _quant("hkv_quant_fp8", k_pages, v_pages, block_table, records, stream)
+
+
+def quant_int4(k_pages, v_pages, block_table, records, stream=None):
+    """Quantize the blocks k/v_pages[:, block_table[b]] into records[:, b] (INT4)."""
+    return _quant("hkv_quant_int4", k_pages, v_pages, block_table, records, stream)
+
+
+def fetch_dequant_rope_shift(records, fmt, block_table, delta_m, rope_base, pairs,
+                             k_pages, v_pages, stream=None):
+    """Dequantize records[:, b], shift keys by delta_m[b], store at page
+    block_table[b] of k/v_pages (dtype of the pages)."""
+    pages, shp, dt = _pages(k_pages, v_pages)
+    L, _, tb, H, d = shp
+    nb = block_table.numel()
+    if records.shape[0] != L or records.shape[1] != nb or delta_m.numel() != nb:
+        raise ValueError("records [L, n_blocks, bytes], table and delta_m must agree")
+    shape = Shape(L, nb, tb, H, d)
+    rec = _records(records)
+    st = lib().hkv_fetch_dequant_rope_shift(
+        ctypes.byref(shape), FORMATS[fmt], ctypes.byref(rec), _i32(block_table, "block_table"),
+        _i32(delta_m, "delta_m"), float(rope_base), PAIRS[pairs], ctypes.byref(pages), dt,
+        _stream(stream, k_pages.device))
+    _check("hkv_fetch_dequant_rope_shift", st)
+    return k_pages, v_pages
+
+
+def crc32_blocks(records, fmt, block_tokens: int, n_kv_heads: int, out=None, stream=None):
+    """CRC-32 of every record; returns a uint32-valued int32 tensor [L, n_blocks]
+    (use `.view(torch.uint32)` or mask with 0xFFFFFFFF after widening)."""
+    L, nb = records.shape[0], records.shape[1]
+    if out is None:
+        out = torch.empty((L, nb), dtype=torch.int32, device=records.device)
+    if out.dtype != torch.int32 or not out.is_contiguous() or out.numel() != L * nb:
+        raise ValueError("out must be a contiguous int32 tensor of L * n_blocks elements")
+    shape = Shape(L, nb, block_tokens, n_kv_heads, HEAD_DIM)
+    rec = _records(records)
+    st = lib().hkv_crc32_blocks(ctypes.byref(shape), FORMATS[fmt], ctypes.byref(rec),
+                                ctypes.c_void_p(out.data_ptr()), _stream(stream, records.device))
+    _check("hkv_crc32_blocks", st)
+    return out

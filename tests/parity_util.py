@@ -1,0 +1,85 @@
+"""Comparison helpers for the GPU parity tests: run the oracle on host
+copies of the same inputs and compare element by element."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle as O
+from quantization_rope_reuse_amd import hkv
+
+TORCH_OF = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+# K tolerance for fp32 pages: max abs error per vector <= 2e-6 * ||k||_2.
+K_REL_TOL = 2e-6
+
+
+def host_f64(t: torch.Tensor) -> np.ndarray:
+    """Exact float64 copy of a GPU tensor of any float dtype."""
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def ulp_of(v: np.ndarray, dtype: str) -> np.ndarray:
+    """Spacing of the page dtype at the oracle's rounded value v."""
+    a = np.abs(v)
+    if dtype == "f16":
+        e = np.maximum(np.floor(np.log2(np.where(a > 0, a, 1.0))), -14)
+        return np.ldexp(1.0, (e - 10).astype(np.int64))
+    if dtype == "bf16":
+        e = np.maximum(np.floor(np.log2(np.where(a > 0, a, 1.0))), -126)
+        return np.ldexp(1.0, (e - 7).astype(np.int64))
+    raise ValueError(dtype)
+
+
+def check_values_exact(gpu: np.ndarray, ref: np.ndarray, what: str):
+    """Bit-exact up to the sign of zero (+0 and -0 compare equal)."""
+    bad = ~((gpu == ref) | (np.isnan(gpu) & np.isnan(ref)))
+    n = int(np.count_nonzero(bad))
+    assert n == 0, f"{what}: {n} of {gpu.size} values differ; first at " \
+                   f"{np.argwhere(bad)[:3].tolist()}: gpu {gpu[bad][:3]} oracle {ref[bad][:3]}"
+
+
+def check_keys(gpu: np.ndarray, exact: np.ndarray, deq: np.ndarray, dtype: str, what: str):
+    """Rotated keys.  fp32 pages: |gpu - exact| <= 2e-6 * ||deq||_2 per
+    vector (exact = the oracle's float64 result).  fp16 / bf16 pages: within
+    one unit in the last place of the oracle's rounded value."""
+    if dtype == "f32":
+        err = np.max(np.abs(gpu - exact), axis=-1)
+        bound = K_REL_TOL * np.sqrt(np.sum(deq * deq, axis=-1))
+        worst = float(np.max(err / np.maximum(bound, 1e-300)))
+        assert np.all(err <= bound), f"{what}: K error up to {worst:.3f} x bound"
+        return worst
+    ref = O.round_output(exact, dtype)
+    d = np.abs(gpu - ref)
+    ok = d <= ulp_of(ref, dtype)
+    n = int(np.count_nonzero(~ok))
+    assert n == 0, f"{what}: {n} K values beyond 1 ulp; e.g. gpu {gpu[~ok][:3]} oracle {ref[~ok][:3]}"
+    return float(np.max(d / ulp_of(ref, dtype)))
+
+
+def compare_fetch_block(k_gpu, v_gpu, kr_exact, vd, kd, out_dtype, dm, what):
+    """One block's fetched pages against the oracle.  V, and K of a block with
+    delta 0, must be exact; other K within tolerance."""
+    check_values_exact(v_gpu, O.round_output(vd, out_dtype), f"{what} V")
+    if dm == 0:
+        check_values_exact(k_gpu, O.round_output(kd, out_dtype), f"{what} K(dm=0)")
+        return 0.0
+    return check_keys(k_gpu, kr_exact, kd, out_dtype, f"{what} K")
+
+
+def crc_u32(t: torch.Tensor) -> np.ndarray:
+    return t.cpu().numpy().view(np.uint32)
+
+
+def canary_fill(t: torch.Tensor):
+    """Fill pages with a NaN bit pattern the codec never produces."""
+    if t.dtype == torch.float32:
+        t.view(torch.int32).fill_(0x7FC0DEAD)
+    else:
+        t.view(torch.int16).fill_(0x7FDA)
+    return t
+
+
+def is_canary(t: torch.Tensor) -> torch.Tensor:
+    if t.dtype == torch.float32:
+        return t.view(torch.int32) == 0x7FC0DEAD
+    return t.view(torch.int16) == 0x7FDA

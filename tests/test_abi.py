@@ -1,0 +1,155 @@
+"""The C-ABI library: it loads, exports every function include/hkv.h
+declares, and rejects bad arguments on the host before any HIP call (these
+tests run without a GPU)."""
+import ctypes
+
+import pytest
+
+from quantization_rope_reuse_amd import hkv
+
+H = hkv
+
+
+def test_exports_every_declared_symbol():
+    names = H.declared_symbols()
+    assert set(names) == {"hkv_quant_fp8", "hkv_quant_int4", "hkv_fetch_dequant_rope_shift",
+                          "hkv_crc32_blocks", "hkv_record_bytes", "hkv_status_string"}
+    lib = H.lib()
+    for n in names:
+        assert getattr(lib, n) is not None
+
+
+def test_record_bytes():
+    assert H.record_bytes("fp8", 64, 8) == 133120
+    assert H.record_bytes("int4", 64, 8) == 67584
+    assert H.record_bytes("fp8", 16, 8) == 33280
+    assert H.record_bytes("int4", 1, 1) == 132
+    assert H.lib().hkv_record_bytes(7, 16, 8, 128) == -1
+    assert H.lib().hkv_record_bytes(0, 16, 8, 64) == -1
+    assert H.lib().hkv_record_bytes(0, 0, 8, 128) == -1
+
+
+def test_status_strings():
+    assert H.status_string(0) == "ok"
+    assert H.status_string(-1) == "invalid argument"
+    assert H.status_string(-2) == "unsupported request"
+    assert H.status_string(-3) == "HIP launch error"
+    assert H.status_string(5) == "unknown status"
+
+
+FAKE = 0x7F0000000000          # a 16-byte aligned address never dereferenced
+
+
+def _shape(**kw):
+    d = dict(n_layers=2, n_blocks=4, block_tokens=16, n_kv_heads=8, head_dim=128)
+    d.update(kw)
+    return H.Shape(**d)
+
+
+def _pages(**kw):
+    d = dict(k=FAKE, v=FAKE + 4096, layer_stride=4 * 16 * 8 * 128, page_stride=16 * 8 * 128,
+             token_stride=8 * 128, head_stride=128, num_pages=4)
+    d.update(kw)
+    return H.Pages(**d)
+
+
+def _recs(**kw):
+    d = dict(base=FAKE, layer_stride_bytes=4 * 33280, block_stride_bytes=33280)
+    d.update(kw)
+    return H.Records(**d)
+
+
+def _quant(shape, pages, dtype, table, recs):
+    return H.lib().hkv_quant_fp8(ctypes.byref(shape) if shape is not None else None,
+                                 ctypes.byref(pages) if pages is not None else None, dtype,
+                                 ctypes.c_void_p(table),
+                                 ctypes.byref(recs) if recs is not None else None, None)
+
+
+def _fetch(shape, recs, table, dm, base, pairs, pages, dtype, fmt=0):
+    return H.lib().hkv_fetch_dequant_rope_shift(
+        ctypes.byref(shape), fmt, ctypes.byref(recs), ctypes.c_void_p(table),
+        ctypes.c_void_p(dm), base, pairs, ctypes.byref(pages), dtype, None)
+
+
+BAD_QUANT = [
+    ("null shape", lambda: _quant(None, _pages(), 0, FAKE, _recs())),
+    ("null pages", lambda: _quant(_shape(), None, 0, FAKE, _recs())),
+    ("null records", lambda: _quant(_shape(), _pages(), 0, FAKE, None)),
+    ("null table", lambda: _quant(_shape(), _pages(), 0, 0, _recs())),
+    ("head_dim 64", lambda: _quant(_shape(head_dim=64), _pages(), 0, FAKE, _recs())),
+    ("zero heads", lambda: _quant(_shape(n_kv_heads=0), _pages(), 0, FAKE, _recs())),
+    ("zero block tokens", lambda: _quant(_shape(block_tokens=0), _pages(), 0, FAKE, _recs())),
+    ("negative layers", lambda: _quant(_shape(n_layers=-1), _pages(), 0, FAKE, _recs())),
+    ("bad dtype", lambda: _quant(_shape(), _pages(), 3, FAKE, _recs())),
+    ("misaligned k", lambda: _quant(_shape(), _pages(k=FAKE + 8), 0, FAKE, _recs())),
+    ("null v", lambda: _quant(_shape(), _pages(v=0), 0, FAKE, _recs())),
+    ("odd head stride", lambda: _quant(_shape(), _pages(head_stride=130), 2, FAKE, _recs())),
+    ("negative stride", lambda: _quant(_shape(), _pages(page_stride=-128), 0, FAKE, _recs())),
+    ("negative num_pages", lambda: _quant(_shape(), _pages(num_pages=-1), 0, FAKE, _recs())),
+    ("misaligned records", lambda: _quant(_shape(), _pages(), 0, FAKE, _recs(base=FAKE + 4))),
+    ("short block stride", lambda: _quant(_shape(), _pages(), 0, FAKE,
+                                          _recs(block_stride_bytes=33264))),
+    ("unaligned block stride", lambda: _quant(_shape(), _pages(), 0, FAKE,
+                                              _recs(block_stride_bytes=33288))),
+]
+
+
+@pytest.mark.parametrize("name,call", BAD_QUANT, ids=[b[0] for b in BAD_QUANT])
+def test_quant_rejects_bad_arguments(name, call):
+    assert call() == H.ERR_INVALID_ARG
+
+
+def test_unsupported_sizes():
+    assert _quant(_shape(n_layers=70000), _pages(), 0, FAKE, _recs()) == H.ERR_UNSUPPORTED
+
+
+def test_empty_calls_launch_nothing():
+    assert _quant(_shape(n_layers=0), _pages(), 0, FAKE, _recs()) == H.OK
+    assert _quant(_shape(n_blocks=0), _pages(), 0, 0, _recs()) == H.OK
+    s = _shape(n_blocks=0)
+    assert _fetch(s, _recs(), 0, 0, 1e4, 0, _pages(), 0) == H.OK
+
+
+BAD_FETCH = [
+    ("zero base", dict(base=0.0)),
+    ("negative base", dict(base=-10000.0)),
+    ("nan base", dict(base=float("nan"))),
+    ("inf base", dict(base=float("inf"))),
+    ("bad pairs", dict(pairs=2)),
+    ("bad format", dict(fmt=2)),
+    ("bad dtype", dict(dtype=-1)),
+    ("null delta", dict(dm=0)),
+    ("null table", dict(table=0)),
+]
+
+
+@pytest.mark.parametrize("name,kw", BAD_FETCH, ids=[b[0] for b in BAD_FETCH])
+def test_fetch_rejects_bad_arguments(name, kw):
+    a = dict(table=FAKE, dm=FAKE, base=1e4, pairs=0, dtype=0, fmt=0)
+    a.update(kw)
+    st = _fetch(_shape(), _recs(), a["table"], a["dm"], a["base"], a["pairs"], _pages(),
+                a["dtype"], a["fmt"])
+    assert st == H.ERR_INVALID_ARG
+
+
+def test_crc_rejects_bad_arguments():
+    lib = H.lib()
+    s, r = _shape(), _recs()
+    assert lib.hkv_crc32_blocks(ctypes.byref(s), 0, ctypes.byref(r), None, None) == H.ERR_INVALID_ARG
+    assert lib.hkv_crc32_blocks(ctypes.byref(s), 9, ctypes.byref(r), ctypes.c_void_p(FAKE),
+                                None) == H.ERR_INVALID_ARG
+    r2 = _recs(base=0)
+    assert lib.hkv_crc32_blocks(ctypes.byref(s), 0, ctypes.byref(r2), ctypes.c_void_p(FAKE),
+                                None) == H.ERR_INVALID_ARG
+
+
+def test_binding_validates_tensors_before_calling():
+    import torch
+    k = torch.zeros((4, 16, 8, 128), dtype=torch.float16)
+    with pytest.raises(ValueError):
+        H.quant_fp8(k, k.float(), torch.zeros(4, dtype=torch.int32),
+                    torch.zeros((1, 4, 33280), dtype=torch.uint8))
+    with pytest.raises(ValueError):
+        H.quant_fp8(k, k, torch.zeros(4, dtype=torch.int64),
+                    torch.zeros((1, 4, 33280), dtype=torch.uint8))

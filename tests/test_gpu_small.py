@@ -1,0 +1,263 @@
+"""GPU parity on the small workloads and the edge cases: the HIP path through
+the C ABI against the CPU oracle on the same seeded inputs.
+
+Bar: record bytes (codes and fp16 scales) and CRCs bit-exact; values, and keys
+of blocks with a zero delta, exact; other keys within 2e-6 * ||k|| (fp32
+pages) or one unit in the last place (fp16 / bf16 pages)."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from parity_util import (TORCH_OF, canary_fill, check_keys, check_values_exact,
+                         compare_fetch_block, crc_u32, host_f64, is_canary)
+from quantization_rope_reuse_amd import hkv
+from quantization_rope_reuse_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def _dev_i32(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(DEV)
+
+
+def _put_both(kp_np, vp_np, table, fmt, src_dtype):
+    """Put on the GPU and in the oracle; return (gpu_records, oracle_records)."""
+    tdt = TORCH_OF[src_dtype]
+    kp = torch.from_numpy(kp_np).to(DEV, tdt)
+    vp = torch.from_numpy(vp_np).to(DEV, tdt)
+    L, nb = kp_np.shape[0], len(table)
+    rec = hkv.alloc_records(L, nb, fmt, kp_np.shape[2], kp_np.shape[3], device=DEV)
+    rec.fill_(0xA5)
+    put = hkv.quant_fp8 if fmt == "fp8" else hkv.quant_int4
+    put(kp, vp, _dev_i32(table), rec)
+    torch.cuda.synchronize()
+    # the oracle takes the values as the GPU saw them (after the dtype cast)
+    ref, live = O.put(host_f64(kp).astype(np.float32), host_f64(vp).astype(np.float32),
+                      table, fmt)
+    return rec, ref, live
+
+
+def _tiny_inputs():
+    w = W.TINY
+    k_pre, v = W.tiny_pre_rope_kv()
+    pos = W.tiny_positions()
+    k_post = O.to_f32(O.rope_apply(k_pre.astype(np.float64), pos, w.rope_base, w.pairs))
+    table = W.put_table(w)
+    kp = W.pages_from_tokens(k_post, w, table)[None]
+    vp = W.pages_from_tokens(v, w, table)[None]
+    return w, kp, vp, table
+
+
+def test_tiny_put_and_crc_bit_exact():
+    w, kp, vp, table = _tiny_inputs()
+    rec, ref, _ = _put_both(kp, vp, table, "fp8", "f32")
+    got = rec.cpu().numpy()
+    assert np.array_equal(got, ref), f"{np.count_nonzero(got != ref)} record bytes differ"
+    crc = hkv.crc32_blocks(rec, "fp8", w.block_tokens, w.n_kv_heads)
+    assert np.array_equal(crc_u32(crc), O.crc32_records(ref))
+
+
+@pytest.mark.parametrize("out_dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("pairs", ["interleaved", "half_split"])
+def test_tiny_fetch(out_dtype, pairs):
+    """Tiny workload: delta 7168 (positions 1024+t -> 8192+t)."""
+    w, kp, vp, table = _tiny_inputs()
+    rec, ref, _ = _put_both(kp, vp, table, "fp8", "f32")
+    dm = W.delta_m(w)
+    ftab = np.array([2, 0, 3, 1], dtype=np.int32)         # a permuted scatter
+    tdt = TORCH_OF[out_dtype]
+    ko = canary_fill(torch.empty((1, 4, 16, 8, 128), dtype=tdt, device=DEV))
+    vo = canary_fill(torch.empty_like(ko))
+    hkv.fetch_dequant_rope_shift(rec, "fp8", _dev_i32(ftab), _dev_i32(dm), w.rope_base, pairs,
+                                 ko, vo)
+    torch.cuda.synchronize()
+    assert not bool(is_canary(ko).any()) and not bool(is_canary(vo).any())
+    kr, vd = O.fetch_exact(ref, "fp8", 16, 8, dm, w.rope_base, pairs)
+    kd, _ = O.dequant_records(ref, "fp8", 16, 8)
+    kg, vg = host_f64(ko), host_f64(vo)
+    for b, page in enumerate(ftab):
+        compare_fetch_block(kg[0, page], vg[0, page], kr[0, b], vd[0, b], kd[0, b], out_dtype,
+                            int(dm[b]), f"block {b}")
+    if pairs == "interleaved" and out_dtype == "f32":
+        # the shifted keys are RoPE at the new positions of the stripped keys
+        pos = W.tiny_positions()
+        deq_tok = kd[0].reshape(64, 8, 128)
+        want = O.rope_apply(O.rope_strip(deq_tok, pos, w.rope_base, pairs), pos + 7168,
+                            w.rope_base, pairs)
+        got_tok = kg[0][ftab].reshape(64, 8, 128)
+        check_keys(got_tok, want, deq_tok, "f32", "RoPE at m_new")
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "int4"])
+def test_gqa_reorder_round_trip(fmt):
+    """4-layer reorder: put gathers from pages in the cached order, fetch
+    scatters in the reused order with deltas 0 and +-512."""
+    w = W.GQA_REORDER
+    L, T, H = w.n_layers, w.n_tokens, w.n_kv_heads
+    cached = np.arange(w.n_blocks, dtype=np.int32)
+    kp = np.stack([W.pages_from_tokens(W.host_layer_values(w, l, 0), w, cached) for l in range(L)])
+    vp = np.stack([W.pages_from_tokens(W.host_layer_values(w, l, 1), w, cached) for l in range(L)])
+    table = W.put_table(w)
+    rec, ref, _ = _put_both(kp, vp, table, fmt, "f32")
+    got = rec.cpu().numpy()
+    assert np.array_equal(got, ref), f"{np.count_nonzero(got != ref)} record bytes differ"
+    crc = hkv.crc32_blocks(rec, fmt, w.block_tokens, H)
+    assert np.array_equal(crc_u32(crc), O.crc32_records(ref))
+    dm = W.delta_m(w)
+    ftab = W.fetch_table(w)
+    ko = canary_fill(torch.empty((L, w.n_blocks, 16, H, 128), dtype=torch.float32, device=DEV))
+    vo = canary_fill(torch.empty_like(ko))
+    hkv.fetch_dequant_rope_shift(rec, fmt, _dev_i32(ftab), _dev_i32(dm), w.rope_base, w.pairs,
+                                 ko, vo)
+    torch.cuda.synchronize()
+    kr, vd = O.fetch_exact(ref, fmt, 16, H, dm, w.rope_base, w.pairs)
+    kd, _ = O.dequant_records(ref, fmt, 16, H)
+    kg, vg = host_f64(ko), host_f64(vo)
+    for b, page in enumerate(ftab):
+        compare_fetch_block(kg[:, page], vg[:, page], kr[:, b], vd[:, b], kd[:, b], "f32",
+                            int(dm[b]), f"{fmt} block {b}")
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "int4"])
+@pytest.mark.parametrize("src_dtype,out_dtype", [("f16", "bf16"), ("bf16", "f16"),
+                                                 ("f32", "f16")])
+def test_ragged_shapes_skips_and_strides(fmt, src_dtype, out_dtype):
+    """Vectors per block not a multiple of the pass size (37 tokens x 9 heads
+    = 333, and 5 x 3 = 15), skipped table entries (negative and beyond the
+    page count), and head-major page layouts given through strides."""
+    rng = np.random.default_rng(61)
+    for tb, H, L, P in ((37, 9, 2, 6), (5, 3, 3, 4)):
+        kp = rng.standard_normal((L, P, tb, H, 128)).astype(np.float32)
+        vp = rng.standard_normal((L, P, tb, H, 128)).astype(np.float32) * 3
+        table = np.array([3, -1, 0, 99, 1][:P + 1], dtype=np.int32)
+        rec, ref, live = _put_both(kp, vp, table, fmt, src_dtype)
+        got = rec.cpu().numpy()
+        for b in range(len(table)):
+            if live[b]:
+                assert np.array_equal(got[:, b], ref[:, b]), f"block {b} differs"
+            else:
+                assert np.all(got[:, b] == 0xA5), f"skipped block {b} was written"
+        assert live.tolist() == [True, False, True, False, True]
+        dm = rng.integers(-30000, 30000, size=len(table)).astype(np.int32)
+        dm[2] = 0
+        # block 0: live but its page is past the buffer; blocks 1, 3 were not put
+        ftab = np.array([P + 3, -1, 0, -1, 2], dtype=np.int32)
+        tdt = TORCH_OF[out_dtype]
+        # head-major pages [L, P, H, T_b, 128] viewed as [L, P, T_b, H, 128]
+        store_k = canary_fill(torch.empty((L, P, H, tb, 128), dtype=tdt, device=DEV))
+        store_v = canary_fill(torch.empty_like(store_k))
+        ko, vo = store_k.transpose(2, 3), store_v.transpose(2, 3)
+        hkv.fetch_dequant_rope_shift(rec, fmt, _dev_i32(ftab), _dev_i32(dm), 10000.0,
+                                     "half_split", ko, vo)
+        torch.cuda.synchronize()
+        kr, vd = O.fetch_exact(ref, fmt, tb, H, dm, 10000.0, "half_split")
+        kd, _ = O.dequant_records(ref, fmt, tb, H)
+        kg, vg = host_f64(ko), host_f64(vo)
+        written = set()
+        for b, page in enumerate(ftab):
+            if page < 0 or page >= P or not live[b]:
+                continue
+            written.add(int(page))
+            compare_fetch_block(kg[:, page], vg[:, page], kr[:, b], vd[:, b], kd[:, b],
+                                out_dtype, int(dm[b]), f"tb={tb} block {b}")
+        canary_k = is_canary(ko).cpu().numpy()
+        for p in range(P):
+            if p in written:
+                assert not canary_k[:, p].any()
+            else:
+                assert canary_k[:, p].all(), f"page {p} was written"
+
+
+def test_scale_edge_cases_fp32_source():
+    """All-zero vectors (with signed zeros), scales that underflow or
+    overflow fp16, and saturation beyond 448."""
+    x = np.zeros((1, 1, 1, 6, 128), np.float32)
+    x[..., 0, 5] = -0.0
+    x[..., 1, :] = 1e-30
+    x[..., 1, 7] = -2e-30
+    x[..., 2, :] = 1e30
+    x[..., 2, 9] = -3e35
+    x[..., 3, :] = np.linspace(-1e-5, 1e-5, 128)
+    x[..., 4, :] = np.linspace(-7e4, 7e4, 128) * 448
+    x[..., 5, :] = 2.0 ** -140                     # fp32 subnormals
+    for fmt in ("fp8", "int4"):
+        rec, ref, _ = _put_both(x, -x, np.array([0], np.int32), fmt, "f32")
+        assert np.array_equal(rec.cpu().numpy(), ref), fmt
+
+
+def test_fp8_encoder_exhaustive_over_reachable_range():
+    """Every fp32 bit pattern of magnitude <= 448, through the FP8 put with an
+    anchor element 448 per vector (scale exactly 1, so the code is the
+    encoding of the element itself), against the oracle's thresholds."""
+    import json
+    import os
+    here = os.path.dirname(os.path.abspath(__file__))
+    with open(os.path.join(here, "golden", "fp8_thresholds.json")) as f:
+        th = torch.tensor(json.load(f)["first_bits_above_code"], dtype=torch.int64, device=DEV)
+    top = 0x43E00000                               # bits of 448.0
+    per_vec = 127
+    n_vec_chunk = 1 << 21                          # 266M patterns per chunk
+    table = None
+    start = 0
+    while start <= top:
+        n = min(per_vec * n_vec_chunk, top + 1 - start)
+        nv = -(-n // per_vec)
+        bits = torch.arange(start, start + nv * per_vec, dtype=torch.int64, device=DEV)
+        bits = torch.clamp(bits, max=top).to(torch.int32)
+        vals = torch.empty((nv, 128), dtype=torch.int32, device=DEV)
+        vals[:, 0] = top
+        vals[:, 1:] = bits.view(nv, per_vec)
+        for sign in (0, 1):
+            v = vals if sign == 0 else vals | torch.tensor(-0x80000000, dtype=torch.int32,
+                                                           device=DEV)
+            src = v.view(torch.float32).view(nv, 1, 1, 128).unsqueeze(0)   # [1, nv, 1, 1, 128]
+            table = torch.arange(nv, dtype=torch.int32, device=DEV)
+            rec = hkv.alloc_records(1, nv, "fp8", 1, 1, device=DEV)
+            hkv.quant_fp8(src, src, table, rec)
+            codes = rec[0, :, 1:128].reshape(-1).to(torch.int64)
+            scales = rec[0, :, 256:258].contiguous().view(torch.int16)
+            assert bool((scales == 0x3C00).all()), "scale is not exactly 1"
+            want = torch.searchsorted(th, bits.to(torch.int64), right=True)
+            if sign:
+                want = want | 0x80
+            bad = codes != want
+            assert not bool(bad.any()), (
+                f"sign {sign}: {int(bad.sum())} mismatches, first pattern "
+                f"{hex(int(bits[bad.nonzero()[0, 0]]))}")
+        start += n
+    assert start > top
+
+
+def test_int4_midpoints_and_range():
+    n = np.arange(-7, 7)
+    x = np.zeros((1, len(n), 1, 1, 128), np.float32)
+    x[0, :, 0, 0, 0] = 7.0
+    x[0, :, 0, 0, 1] = n + 0.5
+    x[0, :, 0, 0, 2] = -(n + 0.5)
+    x[0, :, 0, 0, 3:] = np.linspace(-7, 7, 125)
+    rec, ref, _ = _put_both(x, x, np.arange(len(n), dtype=np.int32), "int4", "f32")
+    assert np.array_equal(rec.cpu().numpy(), ref)
+
+
+def test_side_stream_and_dm_zero_identity():
+    """A launch on a non-default stream; a zero delta returns the
+    dequantized keys exactly for every dtype."""
+    w = W.TINY
+    _, kp, vp, table = _tiny_inputs()
+    rec, ref, _ = _put_both(kp, vp, table, "fp8", "f32")
+    s = torch.cuda.Stream()
+    dm = np.zeros(4, np.int32)
+    for dt in ("f32", "f16", "bf16"):
+        ko = torch.empty((1, 4, 16, 8, 128), dtype=TORCH_OF[dt], device=DEV)
+        vo = torch.empty_like(ko)
+        with torch.cuda.stream(s):
+            hkv.fetch_dequant_rope_shift(rec, "fp8", _dev_i32(table), _dev_i32(dm), 1e4,
+                                         "half_split", ko, vo, stream=s)
+        s.synchronize()
+        kd, vd = O.dequant_records(ref, "fp8", 16, 8)
+        check_values_exact(host_f64(ko)[0], O.round_output(kd[0], dt), f"{dt} K")
+        check_values_exact(host_f64(vo)[0], O.round_output(vd[0], dt), f"{dt} V")

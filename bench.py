@@ -1,0 +1,324 @@
+"""Benchmark of the KV codec hot path on one MI355X.
+
+Workload: a Llama-3-70B-shaped KV cache, 80 layers x 8 KV heads x 128 dims x
+65,536 tokens in bf16 (21.5 GB), blocks of 64 tokens (1,024 pages per layer),
+RoPE base 500000 with split-halves pairs, every block re-used 8,192 positions
+later.  Synthetic standard-normal values drawn on the GPU.
+
+One step is one pass of the whole hot path over that cache:
+  1. put    FP8 E4M3 quantization of all 80 layers, gathered through a
+            permuted block table into per-(layer, block) records (10.9 GB);
+  2. CRC-32 of every record;
+  3. fetch  layer by layer on a side stream (80 launches): dequantize, shift
+            keys by +8192, scatter into a second paged bf16 buffer through
+            another permuted table, visiting blocks in destination-page order
+            (computed once per step by the library's order kernel).
+Inputs are resident in HBM before timing starts.
+
+Reported (one JSON line on stdout):
+  value        algorithmic bytes of the step / step time (GB/s, 1e9 B/s)
+  roofline     the fetch kernel (the dominant one): algorithmic bytes per
+               launch / mean launch time from HIP events on its stream,
+               against 8 TB/s HBM peak; `traffic` = HBM bytes per launch
+               measured with rocprofv3 counters for the current fetch source,
+               else null
+  fetch        fetch-only GB/s, fraction of peak, tokens/s
+  cpu_baseline the CPU oracle on a bounded sample of the same workload
+
+Algorithmic bytes (what the method must move):
+  put    per vector 128 * 2 (bf16 read) + 128 + 2 (codes and scale written),
+         plus the 4-byte table entry per (layer, block);
+  CRC    per record its bytes read plus 4 written;
+  fetch  per vector 128 + 2 read + 128 * 2 written, plus the 4-byte table
+         entry and 4-byte delta per (layer, block).
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "KV fetch GB/s (fp8 dequant+RoPE shift+page scatter), % of HBM peak"
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--cpu-seconds", type=float, default=15.0,
+                   help="approximate budget of the CPU-oracle baseline sample")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--layers", type=int, default=None,
+                   help="override the layer count (profiling runs only)")
+    p.add_argument("--calibrate-copy", action="store_true",
+                   help="also run a plain 1 GiB read + 1 GiB write elementwise kernel "
+                        "(reference for scaling HBM byte counters)")
+    return p.parse_args()
+
+
+def source_digest(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "quantization_rope_reuse_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(per_launch_alg_bytes):
+    """HBM bytes per fetch launch from the committed rocprofv3 counter
+    summary, if it was taken on the current fetch source; else None."""
+    path = os.path.join(ROOT, "profiles", "fetch_llama3_70b_hbm_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    if d.get("source_digest") != source_digest("fetch.hip", "hkv_device.h"):
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(f"bench.py runs on exactly one GPU; --gpus {a.gpus} is not supported "
+              "(the codec shards by layer, head or block with no exchange; see the design "
+              "notes).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from quantization_rope_reuse_amd import hkv
+    from quantization_rope_reuse_amd import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    hkv.lib()                                   # fail loudly if not built
+    dev = torch.device("cuda:0")
+    w = W.LLAMA3_70B
+    L = a.layers or w.n_layers
+    T, H, tb, nb = w.n_tokens, w.n_kv_heads, w.block_tokens, w.n_blocks
+    vecs_per_layer = 2 * T * H                  # K and V
+
+    # ---- inputs resident in HBM -------------------------------------------
+    t0 = time.perf_counter()
+    src_k = torch.empty((L, nb, tb, H, 128), dtype=torch.bfloat16, device=dev)
+    src_v = torch.empty_like(src_k)
+    put_tab = torch.from_numpy(W.put_table(w)).to(dev)
+    ftab = torch.from_numpy(W.fetch_table(w)).to(dev)
+    dm = torch.from_numpy(W.delta_m(w)).to(dev)
+    tmp = torch.empty((T, H, 128), dtype=torch.float32, device=dev)
+    gen = torch.Generator(device=dev)
+    for l in range(L):
+        for kv, dst in ((0, src_k), (1, src_v)):
+            W.device_layer_values(w, l, kv, tmp, generator=gen)
+            dst[l].index_copy_(0, put_tab.long(), tmp.view(nb, tb, H, 128).to(torch.bfloat16))
+    del tmp
+    records = hkv.alloc_records(L, nb, "fp8", tb, H, device=dev)
+    crc = torch.empty((L, nb), dtype=torch.int32, device=dev)
+    order = torch.empty(nb, dtype=torch.int32, device=dev)
+    out_k = torch.empty_like(src_k)
+    out_v = torch.empty_like(src_k)
+    torch.cuda.synchronize()
+    setup_s = time.perf_counter() - t0
+    print(f"[bench] inputs ready: {L} layers, {2 * src_k.numel() * 2 / 1e9:.2f} GB bf16 source, "
+          f"{records.numel() / 1e9:.2f} GB records ({setup_s:.1f} s)", file=sys.stderr, flush=True)
+
+    main_stream = torch.cuda.current_stream(dev)
+    side = torch.cuda.Stream(device=dev)
+    rec_l = [records[l:l + 1] for l in range(L)]
+    ok_l = [out_k[l:l + 1] for l in range(L)]
+    ov_l = [out_v[l:l + 1] for l in range(L)]
+
+    def step(ev=None):
+        # ev: optional HIP events at the phase boundaries (none between the
+        # per-layer fetch launches, which would add a gap between them)
+        if ev is not None:
+            ev[0].record(main_stream)
+        hkv.quant_fp8(src_k, src_v, put_tab, records, stream=main_stream)
+        if ev is not None:
+            ev[1].record(main_stream)
+        hkv.crc32_blocks(records, "fp8", tb, H, out=crc, stream=main_stream)
+        ready = torch.cuda.Event()
+        ready.record(main_stream)
+        side.wait_event(ready)
+        if ev is not None:
+            ev[2].record(side)
+        # blocks listed by destination page, shared by the 80 layer launches
+        hkv.page_visit_order(ftab, nb, out=order, stream=side)
+        for l in range(L):
+            hkv.fetch_dequant_rope_shift(rec_l[l], "fp8", ftab, dm, w.rope_base, w.pairs,
+                                         ok_l[l], ov_l[l], visit_order=order, stream=side)
+        if ev is not None:
+            ev[3].record(side)
+        main_stream.wait_event(ev[3] if ev is not None else _record(side))
+
+    def _record(stream):
+        e = torch.cuda.Event()
+        e.record(stream)
+        return e
+
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(a.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(a.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed * 1e3 / a.steps
+
+    put_ms = [e[0].elapsed_time(e[1]) for e in events]
+    crc_ms = [e[1].elapsed_time(e[2]) for e in events]        # includes the stream hand-off
+    fetch_span_ms = [e[2].elapsed_time(e[3]) for e in events]
+    fetch_ms = [f / L for f in fetch_span_ms]                  # mean per launch
+
+    rb = hkv.record_bytes("fp8", tb, H)
+    put_bytes = L * (vecs_per_layer * (256 + 130) + nb * 4)
+    crc_bytes = L * nb * (rb + 4)
+    fetch_launch_bytes = vecs_per_layer * (130 + 256) + nb * 8
+    fetch_bytes = L * fetch_launch_bytes
+    step_bytes = put_bytes + crc_bytes + fetch_bytes
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+
+    mean_fetch_ms = float(np.mean(fetch_ms))
+    achieved = fetch_launch_bytes / (mean_fetch_ms * 1e-3) / 1e9
+    fetch_gbps = fetch_bytes / (float(np.mean(fetch_span_ms)) * 1e-3) / 1e9
+    tokens_per_s = T / (float(np.mean(fetch_span_ms)) * 1e-3)
+
+    # quick integrity check of the last step: no page left unwritten
+    if bool(torch.isnan(out_k).any()) or bool(torch.isnan(out_v).any()):
+        raise RuntimeError("fetch produced NaN")
+
+    if a.calibrate_copy:
+        # torch.neg over 2**28 fp32 values: reads exactly 1 GiB, writes 1 GiB
+        del src_k, src_v, out_k, out_v, records
+        x = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        y = torch.empty_like(x)
+        for _ in range(3):
+            torch.neg(x, out=y)
+        torch.cuda.synchronize()
+        del x, y
+
+    cpu = None
+    if not a.no_cpu_baseline:
+        cpu = cpu_baseline(w, records_bytes=rb, budget_s=a.cpu_seconds)
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16->fp8->bf16",
+        "data": "synthetic N(0,1), generated on the GPU",
+        "config": {
+            "workload": "Llama-3-70B-shaped KV, one GPU: 80 layers x 8 KV heads x d128 x "
+                        "65536 tokens bf16, blocks of 64, FP8 put + CRC32 + layer-by-layer "
+                        "fetch on a side stream, dm=+8192, RoPE base 500000 split-halves",
+            "layers": L, "tokens": T, "kv_heads": H, "head_dim": 128, "block_tokens": tb,
+            "step_bytes": step_bytes,
+        },
+        "roofline": {
+            "kernel": "fetch_kernel<fp8,bf16,half_split> (one layer per launch)",
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": measured_traffic(fetch_launch_bytes),
+            "alg_bytes_per_launch": fetch_launch_bytes,
+            "mean_launch_ms": round(mean_fetch_ms, 5),
+            "launch_ms_source": "HIP events on the fetch stream around the 80 per-layer "
+                                "launches of each timed step (and the one visit-order "
+                                "launch before them), divided by 80",
+        },
+        "fetch": {
+            "gbps": round(fetch_gbps, 1),
+            "frac_of_peak": round(fetch_gbps / HBM_PEAK_GBPS, 4),
+            "tokens_per_s": round(tokens_per_s, 0),
+            "ms_80_layers": round(float(np.mean(fetch_span_ms)), 4),
+        },
+        "put": {"mean_ms": round(float(np.mean(put_ms)), 4),
+                "gbps": round(put_bytes / (float(np.mean(put_ms)) * 1e-3) / 1e9, 1)},
+        "crc32": {"mean_ms_incl_stream_handoff": round(float(np.mean(crc_ms)), 4),
+                  "gbps": round(crc_bytes / (float(np.mean(crc_ms)) * 1e-3) / 1e9, 1)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(w, records_bytes, budget_s):
+    """The CPU oracle, as it stands, on a bounded sample of the same workload:
+    put + CRC + fetch of the first n blocks of a layer, n doubled until one
+    run takes about a third of `budget_s`, then whole layers added while the
+    total stays under `budget_s`.  Reported in GB/s of the same algorithmic
+    bytes as the GPU figures."""
+    import numpy as np
+
+    import oracle as O
+    from quantization_rope_reuse_amd import workloads as W
+
+    T, H, tb, nb = w.n_tokens, w.n_kv_heads, w.block_tokens, w.n_blocks
+    dm_all = W.delta_m(w)
+
+    def run(layer, n):
+        k_all = W.host_layer_values(w, layer, 0)
+        v_all = W.host_layer_values(w, layer, 1)
+        # the source dtype is bf16: round the drawn values first (input prep)
+        kb = O.f32_to_bf16_value(k_all[: n * tb]).astype(np.float32).reshape(1, n, tb, H, 128)
+        vb = O.f32_to_bf16_value(v_all[: n * tb]).astype(np.float32).reshape(1, n, tb, H, 128)
+        table = np.arange(n)
+        c0 = time.process_time()
+        t0 = time.perf_counter()
+        rec, _ = O.put(kb, vb, table, O.FMT_FP8)
+        O.crc32_records(rec)
+        ko = np.zeros((1, n, tb, H, 128))
+        vo = np.zeros((1, n, tb, H, 128))
+        O.fetch(rec, O.FMT_FP8, tb, H, table, dm_all[:n], w.rope_base, w.pairs, ko, vo, "bf16")
+        return time.perf_counter() - t0, time.process_time() - c0
+
+    n = 4
+    wall, cpu_t = run(0, n)
+    while wall < budget_s / 3 and n < nb:
+        n = min(nb, max(n * 2, int(n * budget_s / 3 / max(wall, 1e-3))))
+        wall, cpu_t = run(0, n)
+    blocks, layers = n, 1
+    while n == nb and wall * (layers + 1) / layers < budget_s and layers < w.n_layers:
+        wl, cl = run(layers, nb)
+        wall, cpu_t, blocks, layers = wall + wl, cpu_t + cl, blocks + nb, layers + 1
+    vecs = 2 * blocks * tb * H
+    alg = (vecs * (256 + 130) + blocks * 4 + blocks * (records_bytes + 4)
+           + vecs * (130 + 256) + blocks * 8)
+    return {
+        "value": round(alg / wall / 1e9, 5),
+        "unit": "GB/s",
+        "cores": max(1, int(round(cpu_t / wall))),
+        "kind": "oracle",
+        "sample": f"put + CRC32 + fetch of {blocks} blocks ({blocks * tb} tokens, {layers} "
+                  f"layer(s)) of the same workload, numpy float64 oracle, {wall:.1f} s wall, "
+                  f"{cpu_t:.1f} s CPU",
+    }
+
+
+if __name__ == "__main__":
+    main()

@@ -145,12 +145,26 @@ int hkv_quant_int4(const hkv_shape* shape, const hkv_pages* src, int32_t src_dty
  *   The result is rounded to nearest even to dst_dtype and stored at page
  *   block_table[b] of `dst`, token t, head h.
  * delta_m: int32 [n_blocks] device array, any sign.
+ * visit_order: NULL, or an int32 [n_blocks] device array holding a
+ *   permutation of 0..n_blocks-1: the order in which blocks are processed.
+ *   The result does not depend on it.  Listing blocks by increasing
+ *   destination page (hkv_page_visit_order) keeps concurrent writes close
+ *   together in HBM; entries outside [0, n_blocks) are skipped.
  * rope_base: finite and > 0. */
 int hkv_fetch_dequant_rope_shift(const hkv_shape* shape, int32_t fmt,
                                  const hkv_records* src, const int32_t* block_table,
-                                 const int32_t* delta_m, double rope_base,
-                                 int32_t pairs, const hkv_pages* dst,
+                                 const int32_t* delta_m, const int32_t* visit_order,
+                                 double rope_base, int32_t pairs, const hkv_pages* dst,
                                  int32_t dst_dtype, hipStream_t stream);
+
+/* Visiting order for hkv_fetch_dequant_rope_shift: writes to order_out
+ * (int32 [n_blocks], device) the logical blocks sorted by destination page
+ * block_table[b]; blocks whose entry is negative or >= num_pages come last,
+ * in index order (ties, which the fetch contract excludes, by index).  This
+ * is a scheduling aid, not a step of the method; O(n_blocks^2) work, meant
+ * for tables of up to a few thousand blocks. */
+int hkv_page_visit_order(const int32_t* block_table, int32_t n_blocks, int32_t num_pages,
+                         int32_t* order_out, hipStream_t stream);
 
 /* CRC-32 of every record (HyperCache post: Part B, the L3-disk line with its
  * per-file CRC32, and the tamper-detection tests of its test-suite section).  The common zlib variant:

@@ -45,13 +45,10 @@ int check_shape(const hkv_shape* s, Geometry* g) {
   g->block_tokens = s->block_tokens;
   g->n_heads = s->n_kv_heads;
   g->vecs = static_cast<int32_t>(vecs);
-  // Up to 256 vectors (8 passes of a 4-wave workgroup) per workgroup.
-  const int32_t per_wg = 256;
-  g->chunks = static_cast<int32_t>((vecs + per_wg - 1) / per_wg);
-  const int64_t even = (vecs + g->chunks - 1) / g->chunks;          // balance the chunks
-  g->vecs_per_chunk = static_cast<int32_t>((even + hkv::kVecsPerPass - 1) /
-                                           hkv::kVecsPerPass * hkv::kVecsPerPass);
-  if (static_cast<int64_t>(s->n_blocks) * 2 * g->chunks > INT32_MAX) return HKV_ERR_UNSUPPORTED;
+  const int64_t per_wg = hkv::kFetchGroupVecs < hkv::kQuantGroupVecs ? hkv::kFetchGroupVecs
+                                                                      : hkv::kQuantGroupVecs;
+  const int64_t chunks = (vecs + per_wg - 1) / per_wg;
+  if (static_cast<int64_t>(s->n_blocks) * 2 * chunks > INT32_MAX) return HKV_ERR_UNSUPPORTED;
   return HKV_OK;
 }
 
@@ -141,8 +138,8 @@ int hkv_quant_int4(const hkv_shape* shape, const hkv_pages* src, int32_t src_dty
 
 int hkv_fetch_dequant_rope_shift(const hkv_shape* shape, int32_t fmt, const hkv_records* src,
                                  const int32_t* block_table, const int32_t* delta_m,
-                                 double rope_base, int32_t pairs, const hkv_pages* dst,
-                                 int32_t dst_dtype, hipStream_t stream) {
+                                 const int32_t* visit_order, double rope_base, int32_t pairs,
+                                 const hkv_pages* dst, int32_t dst_dtype, hipStream_t stream) {
   Geometry g;
   PageView pv;
   RecordView rv;
@@ -156,7 +153,15 @@ int hkv_fetch_dequant_rope_shift(const hkv_shape* shape, int32_t fmt, const hkv_
   if ((!block_table || !delta_m) && g.n_blocks > 0) return HKV_ERR_INVALID_ARG;
   if (g.n_layers == 0 || g.n_blocks == 0) return HKV_OK;
   return to_status(hkv::launch_fetch(fmt, dst_dtype, pairs, g, rv, block_table, delta_m,
-                                     rope_base, pv, stream));
+                                     visit_order, rope_base, pv, stream));
+}
+
+int hkv_page_visit_order(const int32_t* block_table, int32_t n_blocks, int32_t num_pages,
+                         int32_t* order_out, hipStream_t stream) {
+  if (n_blocks < 0 || num_pages < 0) return HKV_ERR_INVALID_ARG;
+  if (n_blocks == 0) return HKV_OK;
+  if (!block_table || !order_out) return HKV_ERR_INVALID_ARG;
+  return to_status(hkv::launch_page_order(block_table, n_blocks, num_pages, order_out, stream));
 }
 
 int hkv_crc32_blocks(const hkv_shape* shape, int32_t fmt, const hkv_records* src,

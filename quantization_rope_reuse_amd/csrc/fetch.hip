@@ -11,15 +11,25 @@
 // моделями и узлами"), module13.py listing, rope_cache / apply_rope.
 //
 // Work decomposition: one workgroup (4 waves) per (layer, block, K|V, chunk of
-// vectors).  Each wave moves 8 vectors per pass, 8 lanes per vector.  Every
-// lane of a key workgroup needs 8 (cos, sin) pairs; the 64 lanes of a wave
-// first compute one pair each (i = lane) in double precision and then gather
-// the 8 they need with cross-lane reads, so the angle setup costs one double
-// sincos per lane per workgroup and no LDS.
+// 64 vectors); each wave owns 16 consecutive vectors and moves them in 2
+// passes of 8 vectors, 8 lanes per vector.  Small workgroups measured best
+// on MI355X (about 16k workgroups per Llama-3-70B-shaped layer).  Every lane
+// of a key workgroup needs 8 (cos, sin) pairs; the 64 lanes of a wave first
+// compute one pair each (i = lane) in double precision and then gather the 8
+// they need with cross-lane reads, so the angle setup costs one double sincos
+// per lane per wave and no LDS.  theta_i is computed once per call on the
+// host, in double.
+//
+// Blocks may be visited in a caller-given order (a permutation of the
+// logical blocks).  Results do not depend on it; listing blocks by
+// increasing destination page makes concurrently running workgroups write
+// neighbouring pages, which measured a few percent faster than visiting a
+// randomly permuted table in logical order.
 //
 // Memory: per vector the kernel reads the codes (128 B FP8 / 64 B INT4) and
-// one fp16 scale, and writes 128 elements of the page dtype.  Loads of the
-// next pass are issued before the current pass is converted and stored.
+// one fp16 scale, and writes 128 elements of the page dtype.  A wave issues
+// the loads of all its passes (and one coalesced load of its scales) before
+// the first store; stores are non-temporal.
 #include "hkv_device.h"
 #include "hkv_launch.h"
 
@@ -31,6 +41,8 @@ struct FetchParams {
   int64_t rec_layer, rec_block;
   const int32_t* table;
   const int32_t* delta;
+  const int32_t* order;      // optional visiting order of the blocks
+  int32_t n_blocks;
   char* k_out;
   char* v_out;
   int64_t o_layer, o_page, o_token, o_head;
@@ -39,17 +51,16 @@ struct FetchParams {
   int32_t vecs;
   int32_t chunks;
   int32_t vecs_per_chunk;
-  double rope_base;
+  double theta[kHeadDim / 2];   // 1 / base^(2i/128), computed on the host in double
 };
 
-template <int FMT> struct RawVec;
-template <> struct RawVec<kFP8> { u32x2 lo, hi; uint32_t scale; };
-template <> struct RawVec<kINT4> { uint32_t lo, hi; uint32_t scale; };
+template <int FMT> struct RawCodes;
+template <> struct RawCodes<kFP8> { u32x2 lo, hi; };
+template <> struct RawCodes<kINT4> { uint32_t lo, hi; };
 
 template <int FMT>
-__device__ __forceinline__ RawVec<FMT> load_vec(const uint8_t* codes, const uint16_t* scales,
-                                                int v, int sub) {
-  RawVec<FMT> r;
+__device__ __forceinline__ RawCodes<FMT> load_codes(const uint8_t* codes, int v, int sub) {
+  RawCodes<FMT> r;
   if constexpr (FMT == kFP8) {
     const uint8_t* c = codes + static_cast<int64_t>(v) * kHeadDim + 8 * sub;
     r.lo = *reinterpret_cast<const u32x2*>(c);
@@ -59,12 +70,12 @@ __device__ __forceinline__ RawVec<FMT> load_vec(const uint8_t* codes, const uint
     r.lo = *reinterpret_cast<const uint32_t*>(c);
     r.hi = *reinterpret_cast<const uint32_t*>(c + 32);
   }
-  r.scale = scales[v];
   return r;
 }
 
 template <int FMT>
-__device__ __forceinline__ void dequant(const RawVec<FMT>& r, float (&a)[8], float (&b)[8]) {
+__device__ __forceinline__ void dequant(const RawCodes<FMT>& r, float s, float (&a)[8],
+                                        float (&b)[8]) {
   if constexpr (FMT == kFP8) {
     fp8x8_to_f32(r.lo, a);
     fp8x8_to_f32(r.hi, b);
@@ -72,7 +83,6 @@ __device__ __forceinline__ void dequant(const RawVec<FMT>& r, float (&a)[8], flo
     int4x8_to_f32(r.lo, a);
     int4x8_to_f32(r.hi, b);
   }
-  const float s = f16_bits_to_f32(r.scale);
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     a[j] *= s;   // exact: at most 4 + 11 significant bits
@@ -87,13 +97,21 @@ __device__ __forceinline__ void rot(float& x, float& y, float c, float s) {
   y = ny;
 }
 
+// Each wave owns kFetchPasses * 8 consecutive vectors of its workgroup's
+// chunk and moves them in kFetchPasses passes of 8.  All loads of the wave
+// are issued before its first store: one counter tracks a wave's loads and
+// stores in issue order, so a load issued after a store could not be waited
+// for without also waiting for that store.  Stores are non-temporal: the
+// pages are not read again by this kernel.
 template <int FMT, int ODT, int PAIRS>
 __global__ __launch_bounds__(kThreads) void fetch_kernel(FetchParams p) {
   const int layer = blockIdx.y;
   const int chunk = blockIdx.x % p.chunks;
   const int bk = blockIdx.x / p.chunks;
   const int kv = bk & 1;
-  const int blk = bk >> 1;
+  const int slot = bk >> 1;
+  const int blk = p.order ? p.order[slot] : slot;
+  if (blk < 0 || blk >= p.n_blocks) return;
   const int page = p.table[blk];
   if (page < 0 || page >= p.num_pages) return;
 
@@ -109,21 +127,31 @@ __global__ __launch_bounds__(kThreads) void fetch_kernel(FetchParams p) {
   const int wave = threadIdx.x / kWave;
   const int sub = lane & (kLanesPerVec - 1);
   const int vsub = lane / kLanesPerVec;
-  const int v_begin = chunk * p.vecs_per_chunk;
-  const int v_end = min(v_begin + p.vecs_per_chunk, p.vecs);
+  constexpr int kWaveVecs = kVecsPerWave * kFetchPasses;
+  const int v_end = min((chunk + 1) * p.vecs_per_chunk, p.vecs);
+  const int v0 = chunk * p.vecs_per_chunk + wave * kWaveVecs;
+  if (v0 >= v_end) return;                      // whole wave idle
 
-  int v = v_begin + wave * kVecsPerWave + vsub;
-  RawVec<FMT> cur;
-  if (v < v_end) cur = load_vec<FMT>(codes, scales, v, sub);
+  // Lane L holds the scale of vector v0 + (L mod kWaveVecs).
+  const int sv = v0 + (lane % kWaveVecs);
+  uint32_t my_scale = 0;
+  if (sv < v_end) my_scale = scales[sv];
+  RawCodes<FMT> raw[kFetchPasses];
+#pragma unroll
+  for (int i = 0; i < kFetchPasses; ++i) {
+    const int v = v0 + kVecsPerWave * i + vsub;
+    if (v < v_end) raw[i] = load_codes<FMT>(codes, v, sub);
+  }
 
-  // Angle setup for keys with a nonzero delta (uniform per workgroup).
+  // Angle setup for keys with a nonzero delta (uniform per workgroup),
+  // overlapping the loads above: lane i forms phi_i = dm * theta_i and its
+  // cos / sin in double precision (full range reduction), rounded to fp32.
   const int dm = kv == 0 ? p.delta[blk] : 0;
   const bool rotate = dm != 0;
   float cs[8], sn[8];
   if (rotate) {
-    const double theta = 1.0 / pow(p.rope_base, static_cast<double>(2 * lane) / kHeadDim);
     double sd, cd;
-    sincos(static_cast<double>(dm) * theta, &sd, &cd);
+    sincos(static_cast<double>(dm) * p.theta[lane], &sd, &cd);
     const float cf = static_cast<float>(cd);
     const float sf = static_cast<float>(sd);
 #pragma unroll
@@ -138,39 +166,37 @@ __global__ __launch_bounds__(kThreads) void fetch_kernel(FetchParams p) {
     }
   }
 
-  while (v < v_end) {
-    const int vn = v + kVecsPerPass;
-    RawVec<FMT> nxt;
-    if (vn < v_end) nxt = load_vec<FMT>(codes, scales, vn, sub);
-
-    float a[8], b[8];
-    dequant<FMT>(cur, a, b);
-    if (rotate) {
-      if constexpr (PAIRS == kInterleaved) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          rot(a[2 * j], a[2 * j + 1], cs[j], sn[j]);
-          rot(b[2 * j], b[2 * j + 1], cs[4 + j], sn[4 + j]);
+  for (int i = 0; i < kFetchPasses; ++i) {
+    const int v = v0 + kVecsPerWave * i + vsub;
+    const float s = f16_bits_to_f32(__shfl(my_scale, kVecsPerWave * i + vsub));
+    if (v < v_end) {
+      float a[8], b[8];
+      dequant<FMT>(raw[i], s, a, b);
+      if (rotate) {
+        if constexpr (PAIRS == kInterleaved) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            rot(a[2 * j], a[2 * j + 1], cs[j], sn[j]);
+            rot(b[2 * j], b[2 * j + 1], cs[4 + j], sn[4 + j]);
+          }
+        } else {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) rot(a[j], b[j], cs[j], sn[j]);
         }
-      } else {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) rot(a[j], b[j], cs[j], sn[j]);
       }
+      const int t = v / p.n_heads;
+      const int h = v - t * p.n_heads;
+      char* dst = out + t * p.o_token + h * p.o_head + 8 * sub * ES;
+      store8<ODT, true>(dst, a);
+      store8<ODT, true>(dst + 64 * ES, b);
     }
-    const int t = v / p.n_heads;
-    const int h = v - t * p.n_heads;
-    char* dst = out + t * p.o_token + h * p.o_head + 8 * sub * ES;
-    store8<ODT>(dst, a);
-    store8<ODT>(dst + 64 * ES, b);
-
-    cur = nxt;
-    v = vn;
   }
 }
 
 template <int FMT, int ODT, int PAIRS>
 hipError_t launch_t(const FetchParams& p, const Geometry& g, hipStream_t stream) {
-  dim3 grid(static_cast<unsigned>(g.n_blocks) * 2u * static_cast<unsigned>(g.chunks),
+  dim3 grid(static_cast<unsigned>(g.n_blocks) * 2u * static_cast<unsigned>(p.chunks),
             static_cast<unsigned>(g.n_layers));
   hipLaunchKernelGGL((fetch_kernel<FMT, ODT, PAIRS>), grid, dim3(kThreads), 0, stream, p);
   return hipGetLastError();
@@ -196,13 +222,16 @@ hipError_t launch_dtype(int odt, int pairs, const FetchParams& p, const Geometry
 
 hipError_t launch_fetch(int fmt, int dst_dtype, int pairs, const Geometry& g,
                         const RecordView& src, const int32_t* table, const int32_t* delta_m,
-                        double rope_base, const PageView& dst, hipStream_t stream) {
+                        const int32_t* visit_order, double rope_base, const PageView& dst,
+                        hipStream_t stream) {
   FetchParams p;
   p.rec = src.base;
   p.rec_layer = src.layer;
   p.rec_block = src.block;
   p.table = table;
   p.delta = delta_m;
+  p.order = visit_order;
+  p.n_blocks = g.n_blocks;
   p.k_out = dst.k;
   p.v_out = dst.v;
   p.o_layer = dst.layer;
@@ -212,9 +241,11 @@ hipError_t launch_fetch(int fmt, int dst_dtype, int pairs, const Geometry& g,
   p.num_pages = dst.num_pages;
   p.n_heads = g.n_heads;
   p.vecs = g.vecs;
-  p.chunks = g.chunks;
-  p.vecs_per_chunk = g.vecs_per_chunk;
-  p.rope_base = rope_base;
+  // Workgroups of kFetchGroupVecs vectors (4 waves x kFetchPasses passes).
+  p.chunks = (g.vecs + kFetchGroupVecs - 1) / kFetchGroupVecs;
+  p.vecs_per_chunk = kFetchGroupVecs;
+  for (int i = 0; i < kHeadDim / 2; ++i)
+    p.theta[i] = 1.0 / pow(rope_base, static_cast<double>(2 * i) / kHeadDim);
   return fmt == kFP8 ? launch_dtype<kFP8>(dst_dtype, pairs, p, g, stream)
                      : launch_dtype<kINT4>(dst_dtype, pairs, p, g, stream);
 }

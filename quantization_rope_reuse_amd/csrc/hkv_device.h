@@ -20,6 +20,10 @@ constexpr int kWave = 64;
 constexpr int kThreads = 256;                          // 4 waves per workgroup
 constexpr int kVecsPerWave = kWave / kLanesPerVec;     // 8
 constexpr int kVecsPerPass = kThreads / kLanesPerVec;  // 32
+constexpr int kFetchPasses = 2;                        // fetch: passes per wave
+constexpr int kFetchGroupVecs = kVecsPerWave * kFetchPasses * (kThreads / kWave);   // 64
+constexpr int kQuantPasses = 2;                        // put: passes per wave
+constexpr int kQuantGroupVecs = kVecsPerWave * kQuantPasses * (kThreads / kWave);   // 64
 
 enum DType { kF32 = 0, kF16 = 1, kBF16 = 2 };
 enum Format { kFP8 = 0, kINT4 = 1 };
@@ -91,7 +95,17 @@ __device__ __forceinline__ void load8(const char* p, float (&x)[8]) {
   }
 }
 
-template <int DT>
+template <bool NT>
+__device__ __forceinline__ void store16(char* p, u32x4 v) {
+  if constexpr (NT)
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+  else
+    *reinterpret_cast<u32x4*>(p) = v;
+}
+
+// Store 8 fp32 values as the page dtype (round to nearest even); NT selects
+// non-temporal stores.
+template <int DT, bool NT = false>
 __device__ __forceinline__ void store8(char* p, const float (&x)[8]) {
   if constexpr (DT == kF32) {
     u32x4 a, b;
@@ -102,8 +116,8 @@ __device__ __forceinline__ void store8(char* p, const float (&x)[8]) {
       a[j] = __builtin_bit_cast(uint32_t, fa);
       b[j] = __builtin_bit_cast(uint32_t, fb);
     }
-    *reinterpret_cast<u32x4*>(p) = a;
-    *reinterpret_cast<u32x4*>(p + 16) = b;
+    store16<NT>(p, a);
+    store16<NT>(p + 16, b);
   } else {
     u32x4 a;
 #pragma unroll
@@ -118,7 +132,7 @@ __device__ __forceinline__ void store8(char* p, const float (&x)[8]) {
       }
       a[j] = lo | (hi << 16);
     }
-    *reinterpret_cast<u32x4*>(p) = a;
+    store16<NT>(p, a);
   }
 }
 

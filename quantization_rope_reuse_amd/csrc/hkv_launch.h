@@ -15,8 +15,6 @@ struct Geometry {
   int32_t block_tokens;
   int32_t n_heads;
   int32_t vecs;            // block_tokens * n_heads vectors per (block, K|V)
-  int32_t chunks;          // workgroups per (layer, block, K|V)
-  int32_t vecs_per_chunk;  // multiple of kVecsPerPass (32)
 };
 
 struct PageView {          // byte addressing of a paged buffer
@@ -36,7 +34,11 @@ hipError_t launch_quant(int fmt, int src_dtype, const Geometry& g, const PageVie
 
 hipError_t launch_fetch(int fmt, int dst_dtype, int pairs, const Geometry& g,
                         const RecordView& src, const int32_t* table, const int32_t* delta_m,
-                        double rope_base, const PageView& dst, hipStream_t stream);
+                        const int32_t* visit_order, double rope_base, const PageView& dst,
+                        hipStream_t stream);
+
+hipError_t launch_page_order(const int32_t* table, int32_t n_blocks, int32_t num_pages,
+                             int32_t* order, hipStream_t stream);
 
 hipError_t launch_crc32(const Geometry& g, int64_t record_bytes, const RecordView& src,
                         uint32_t* out, hipStream_t stream);

@@ -10,9 +10,10 @@
 //   INT4; IEEE fp32 division); code_j = round(x_j / s) to E4M3 (saturating
 //   at +-448) or to an integer clamped to [-7, 7].
 //
-// Work decomposition matches the fetch kernel: one workgroup per (layer,
-// block, K|V, chunk), 8 lanes per vector; the vector's amax is reduced over
-// its 8 lanes with cross-lane max.
+// Work decomposition: one workgroup (4 waves) per (layer, block, K|V, chunk
+// of kQuantGroupVecs vectors), kQuantPasses * 8 consecutive vectors per wave,
+// 8 lanes per vector; the vector's amax is reduced over its 8 lanes with
+// cross-lane max.
 #include "hkv_device.h"
 #include "hkv_launch.h"
 
@@ -45,6 +46,88 @@ __device__ __forceinline__ uint32_t scale_bits(float amax) {
   return h;
 }
 
+// Source run of 8 elements (lane-owned half of a vector) as raw words.
+template <int SDT> struct RawSrc;
+template <> struct RawSrc<kF32> { u32x4 w0, w1; };
+template <> struct RawSrc<kF16> { u32x4 w0; };
+template <> struct RawSrc<kBF16> { u32x4 w0; };
+
+template <int SDT>
+__device__ __forceinline__ RawSrc<SDT> load_run(const char* p) {
+  RawSrc<SDT> r;
+  r.w0 = *reinterpret_cast<const u32x4*>(p);
+  if constexpr (SDT == kF32) r.w1 = *reinterpret_cast<const u32x4*>(p + 16);
+  return r;
+}
+
+template <int SDT>
+__device__ __forceinline__ void run_to_f32(const RawSrc<SDT>& r, float (&x)[8]) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t w = r.w0[j];
+    if constexpr (SDT == kF32) {
+      const uint32_t w1 = r.w1[j];
+      x[j] = __builtin_bit_cast(float, w);
+      x[4 + j] = __builtin_bit_cast(float, w1);
+    } else if constexpr (SDT == kF16) {
+      x[2 * j] = f16_bits_to_f32(w & 0xFFFFu);
+      x[2 * j + 1] = f16_bits_to_f32(w >> 16);
+    } else {
+      x[2 * j] = bf16_bits_to_f32(w & 0xFFFFu);
+      x[2 * j + 1] = bf16_bits_to_f32(w >> 16);
+    }
+  }
+}
+
+// Quantize one vector's lane-owned runs a (elements 8s..8s+7) and b
+// (64+8s..64+8s+7); returns the fp16 scale bits (same in all 8 lanes).
+template <int FMT>
+__device__ __forceinline__ uint32_t quant_vector(float (&a)[8], float (&b)[8], uint8_t* c_ptr,
+                                                 int sub, bool active) {
+  float m = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) m = fmaxf(m, fmaxf(fabsf(a[j]), fabsf(b[j])));
+  const float amax = max_over_vector_lanes(m);
+  constexpr int QMAX = FMT == kFP8 ? 448 : 7;
+  const uint32_t sbits = scale_bits<QMAX>(amax);
+  if (!active) return sbits;
+  const float s = f16_bits_to_f32(sbits);
+  const bool zero_scale = sbits == 0u;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    a[j] = zero_scale ? a[j] : a[j] / s;                // IEEE division
+    b[j] = zero_scale ? b[j] : b[j] / s;
+  }
+  if constexpr (FMT == kFP8) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      a[j] = fminf(fmaxf(a[j], -448.0f), 448.0f);
+      b[j] = fminf(fmaxf(b[j], -448.0f), 448.0f);
+    }
+    __builtin_nontemporal_store(f32x8_to_fp8(a), reinterpret_cast<u32x2*>(c_ptr + 8 * sub));
+    __builtin_nontemporal_store(f32x8_to_fp8(b), reinterpret_cast<u32x2*>(c_ptr + 64 + 8 * sub));
+  } else {
+    uint32_t wa = 0, wb = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int ia = static_cast<int>(fminf(fmaxf(rintf(a[j]), -7.0f), 7.0f));
+      const int ib = static_cast<int>(fminf(fmaxf(rintf(b[j]), -7.0f), 7.0f));
+      wa |= (static_cast<uint32_t>(ia) & 0xFu) << (4 * j);
+      wb |= (static_cast<uint32_t>(ib) & 0xFu) << (4 * j);
+    }
+    __builtin_nontemporal_store(wa, reinterpret_cast<uint32_t*>(c_ptr + 4 * sub));
+    __builtin_nontemporal_store(wb, reinterpret_cast<uint32_t*>(c_ptr + 32 + 4 * sub));
+  }
+  return sbits;
+}
+
+// Each wave owns kQuantPasses * 8 consecutive vectors of its workgroup's
+// chunk, moved in passes of 8 vectors.  Source loads are issued a batch of
+// passes at a time before any store of the batch: one counter tracks a
+// wave's loads and stores in issue order, so loads issued after a store
+// cannot be waited for without also waiting for the store.  Lane L collects
+// the scale of vector v0 + L and stores it once at the end.  Record stores
+// are non-temporal.
 template <int FMT, int SDT>
 __global__ __launch_bounds__(kThreads) void quant_kernel(QuantParams p) {
   const int layer = blockIdx.y;
@@ -57,6 +140,8 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(QuantParams p) {
 
   constexpr int CB = FMT == kFP8 ? kHeadDim : kHeadDim / 2;
   constexpr int ES = ElemSize<SDT>::value;
+  constexpr int kBatch = SDT == kF32 ? (kQuantPasses < 4 ? kQuantPasses : 4) : kQuantPasses;
+  constexpr int kWaveVecs = kVecsPerWave * kQuantPasses;
   const char* src = (kv ? p.v_src : p.k_src) + layer * p.s_layer + page * p.s_page;
   uint8_t* rec = p.rec + layer * p.rec_layer + blk * p.rec_block;
   uint8_t* codes = rec + static_cast<int64_t>(kv) * p.vecs * CB;
@@ -66,62 +151,50 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(QuantParams p) {
   const int wave = threadIdx.x / kWave;
   const int sub = lane & (kLanesPerVec - 1);
   const int vsub = lane / kLanesPerVec;
-  const int v_begin = chunk * p.vecs_per_chunk;
-  const int v_end = min(v_begin + p.vecs_per_chunk, p.vecs);
+  const int v_end = min((chunk + 1) * p.vecs_per_chunk, p.vecs);
+  const int v0 = chunk * p.vecs_per_chunk + wave * kWaveVecs;
+  if (v0 >= v_end) return;                      // whole wave idle
 
-  for (int v = v_begin + wave * kVecsPerWave + vsub; v < v_end; v += kVecsPerPass) {
-    const int t = v / p.n_heads;
-    const int h = v - t * p.n_heads;
-    const char* x_ptr = src + t * p.s_token + h * p.s_head + 8 * sub * ES;
-    float a[8], b[8];
-    load8<SDT>(x_ptr, a);
-    load8<SDT>(x_ptr + 64 * ES, b);
-
-    float m = 0.0f;
+  uint32_t my_scale = 0;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) m = fmaxf(m, fmaxf(fabsf(a[j]), fabsf(b[j])));
-    const float amax = max_over_vector_lanes(m);
-
-    constexpr int QMAX = FMT == kFP8 ? 448 : 7;
-    const uint32_t sbits = scale_bits<QMAX>(amax);
-    const float s = f16_bits_to_f32(sbits);
-    const bool zero_scale = sbits == 0u;
-
-    float qa[8], qb[8];
+  for (int i0 = 0; i0 < kQuantPasses; i0 += kBatch) {
+    RawSrc<SDT> ra[kBatch], rb[kBatch];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      qa[j] = zero_scale ? a[j] : a[j] / s;            // IEEE division
-      qb[j] = zero_scale ? b[j] : b[j] / s;
-    }
-
-    uint8_t* c_ptr = codes + static_cast<int64_t>(v) * CB;
-    if constexpr (FMT == kFP8) {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        qa[j] = fminf(fmaxf(qa[j], -448.0f), 448.0f);
-        qb[j] = fminf(fmaxf(qb[j], -448.0f), 448.0f);
+    for (int i = 0; i < kBatch; ++i) {
+      const int v = v0 + kVecsPerWave * (i0 + i) + vsub;
+      if (v < v_end) {
+        const int t = v / p.n_heads;
+        const int h = v - t * p.n_heads;
+        const char* x_ptr = src + t * p.s_token + h * p.s_head + 8 * sub * ES;
+        ra[i] = load_run<SDT>(x_ptr);
+        rb[i] = load_run<SDT>(x_ptr + 64 * ES);
       }
-      *reinterpret_cast<u32x2*>(c_ptr + 8 * sub) = f32x8_to_fp8(qa);
-      *reinterpret_cast<u32x2*>(c_ptr + 64 + 8 * sub) = f32x8_to_fp8(qb);
-    } else {
-      uint32_t wa = 0, wb = 0;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int ia = static_cast<int>(fminf(fmaxf(rintf(qa[j]), -7.0f), 7.0f));
-        const int ib = static_cast<int>(fminf(fmaxf(rintf(qb[j]), -7.0f), 7.0f));
-        wa |= (static_cast<uint32_t>(ia) & 0xFu) << (4 * j);
-        wb |= (static_cast<uint32_t>(ib) & 0xFu) << (4 * j);
-      }
-      *reinterpret_cast<uint32_t*>(c_ptr + 4 * sub) = wa;
-      *reinterpret_cast<uint32_t*>(c_ptr + 32 + 4 * sub) = wb;
     }
-    if (sub == 0) scales[v] = static_cast<uint16_t>(sbits);
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      const int v = v0 + kVecsPerWave * (i0 + i) + vsub;
+      const bool active = v < v_end;
+      float a[8], b[8];
+      if (active) {
+        run_to_f32<SDT>(ra[i], a);
+        run_to_f32<SDT>(rb[i], b);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) a[j] = b[j] = 0.0f;
+      }
+      const uint32_t sbits = quant_vector<FMT>(a, b, codes + static_cast<int64_t>(v) * CB, sub,
+                                               active);
+      // lane 8*(i0+i) + r keeps the scale of vector r of this pass
+      const uint32_t got = __shfl(sbits, (lane & 7) * kLanesPerVec);
+      if (lane / kLanesPerVec == i0 + i) my_scale = got;
+    }
   }
+  if (lane < kWaveVecs && v0 + lane < v_end) scales[v0 + lane] = static_cast<uint16_t>(my_scale);
 }
 
 template <int FMT, int SDT>
 hipError_t launch_t(const QuantParams& p, const Geometry& g, hipStream_t stream) {
-  dim3 grid(static_cast<unsigned>(g.n_blocks) * 2u * static_cast<unsigned>(g.chunks),
+  dim3 grid(static_cast<unsigned>(g.n_blocks) * 2u * static_cast<unsigned>(p.chunks),
             static_cast<unsigned>(g.n_layers));
   hipLaunchKernelGGL((quant_kernel<FMT, SDT>), grid, dim3(kThreads), 0, stream, p);
   return hipGetLastError();
@@ -154,8 +227,8 @@ hipError_t launch_quant(int fmt, int src_dtype, const Geometry& g, const PageVie
   p.rec_block = dst.block;
   p.n_heads = g.n_heads;
   p.vecs = g.vecs;
-  p.chunks = g.chunks;
-  p.vecs_per_chunk = g.vecs_per_chunk;
+  p.chunks = (g.vecs + kQuantGroupVecs - 1) / kQuantGroupVecs;
+  p.vecs_per_chunk = kQuantGroupVecs;
   return fmt == kFP8 ? launch_dtype<kFP8>(src_dtype, p, g, stream)
                      : launch_dtype<kINT4>(src_dtype, p, g, stream);
 }

@@ -80,11 +80,12 @@ def lib():
         l.hkv_quant_fp8.argtypes = [P(Shape), P(Pages), ctypes.c_int32, vp, P(Records), vp]
         l.hkv_quant_int4.argtypes = [P(Shape), P(Pages), ctypes.c_int32, vp, P(Records), vp]
         l.hkv_fetch_dequant_rope_shift.argtypes = [
-            P(Shape), ctypes.c_int32, P(Records), vp, vp, ctypes.c_double, ctypes.c_int32,
+            P(Shape), ctypes.c_int32, P(Records), vp, vp, vp, ctypes.c_double, ctypes.c_int32,
             P(Pages), ctypes.c_int32, vp]
+        l.hkv_page_visit_order.argtypes = [vp, ctypes.c_int32, ctypes.c_int32, vp, vp]
         l.hkv_crc32_blocks.argtypes = [P(Shape), ctypes.c_int32, P(Records), vp, vp]
         for name in ("hkv_quant_fp8", "hkv_quant_int4", "hkv_fetch_dequant_rope_shift",
-                     "hkv_crc32_blocks"):
+                     "hkv_crc32_blocks", "hkv_page_visit_order"):
             getattr(l, name).restype = ctypes.c_int
         l.hkv_record_bytes.argtypes = [ctypes.c_int32] * 4
         l.hkv_record_bytes.restype = ctypes.c_int64
@@ -192,22 +193,40 @@ def quant_int4(k_pages, v_pages, block_table, records, stream=None):
 
 
 def fetch_dequant_rope_shift(records, fmt, block_table, delta_m, rope_base, pairs,
-                             k_pages, v_pages, stream=None):
+                             k_pages, v_pages, visit_order=None, stream=None):
     """Dequantize records[:, b], shift keys by delta_m[b], store at page
-    block_table[b] of k/v_pages (dtype of the pages)."""
+    block_table[b] of k/v_pages (dtype of the pages).  visit_order: optional
+    int32 permutation of the blocks (see page_visit_order)."""
     pages, shp, dt = _pages(k_pages, v_pages)
     L, _, tb, H, d = shp
     nb = block_table.numel()
     if records.shape[0] != L or records.shape[1] != nb or delta_m.numel() != nb:
         raise ValueError("records [L, n_blocks, bytes], table and delta_m must agree")
+    if visit_order is not None and visit_order.numel() != nb:
+        raise ValueError("visit_order must hold n_blocks entries")
     shape = Shape(L, nb, tb, H, d)
     rec = _records(records)
+    order = None if visit_order is None else _i32(visit_order, "visit_order")
     st = lib().hkv_fetch_dequant_rope_shift(
         ctypes.byref(shape), FORMATS[fmt], ctypes.byref(rec), _i32(block_table, "block_table"),
-        _i32(delta_m, "delta_m"), float(rope_base), PAIRS[pairs], ctypes.byref(pages), dt,
-        _stream(stream, k_pages.device))
+        _i32(delta_m, "delta_m"), order, float(rope_base), PAIRS[pairs], ctypes.byref(pages),
+        dt, _stream(stream, k_pages.device))
     _check("hkv_fetch_dequant_rope_shift", st)
     return k_pages, v_pages
+
+
+def page_visit_order(block_table, num_pages: int, out=None, stream=None):
+    """Blocks listed by increasing destination page (skipped blocks last):
+    an int32 tensor [n_blocks] for fetch_dequant_rope_shift's visit_order."""
+    nb = block_table.numel()
+    if out is None:
+        out = torch.empty(nb, dtype=torch.int32, device=block_table.device)
+    if out.numel() != nb:
+        raise ValueError("out must hold n_blocks entries")
+    st = lib().hkv_page_visit_order(_i32(block_table, "block_table"), nb, int(num_pages),
+                                    _i32(out, "out"), _stream(stream, block_table.device))
+    _check("hkv_page_visit_order", st)
+    return out
 
 
 def crc32_blocks(records, fmt, block_tokens: int, n_kv_heads: int, out=None, stream=None):

@@ -13,7 +13,8 @@ H = hkv
 def test_exports_every_declared_symbol():
     names = H.declared_symbols()
     assert set(names) == {"hkv_quant_fp8", "hkv_quant_int4", "hkv_fetch_dequant_rope_shift",
-                          "hkv_crc32_blocks", "hkv_record_bytes", "hkv_status_string"}
+                          "hkv_crc32_blocks", "hkv_record_bytes", "hkv_status_string",
+                          "hkv_page_visit_order"}
     lib = H.lib()
     for n in names:
         assert getattr(lib, n) is not None
@@ -69,7 +70,7 @@ def _quant(shape, pages, dtype, table, recs):
 def _fetch(shape, recs, table, dm, base, pairs, pages, dtype, fmt=0):
     return H.lib().hkv_fetch_dequant_rope_shift(
         ctypes.byref(shape), fmt, ctypes.byref(recs), ctypes.c_void_p(table),
-        ctypes.c_void_p(dm), base, pairs, ctypes.byref(pages), dtype, None)
+        ctypes.c_void_p(dm), None, base, pairs, ctypes.byref(pages), dtype, None)
 
 
 BAD_QUANT = [
@@ -142,6 +143,15 @@ def test_crc_rejects_bad_arguments():
     r2 = _recs(base=0)
     assert lib.hkv_crc32_blocks(ctypes.byref(s), 0, ctypes.byref(r2), ctypes.c_void_p(FAKE),
                                 None) == H.ERR_INVALID_ARG
+
+
+def test_page_order_rejects_bad_arguments():
+    lib = H.lib()
+    assert lib.hkv_page_visit_order(None, 4, 4, ctypes.c_void_p(FAKE), None) == H.ERR_INVALID_ARG
+    assert lib.hkv_page_visit_order(ctypes.c_void_p(FAKE), 4, 4, None, None) == H.ERR_INVALID_ARG
+    assert lib.hkv_page_visit_order(ctypes.c_void_p(FAKE), -1, 4, ctypes.c_void_p(FAKE),
+                                    None) == H.ERR_INVALID_ARG
+    assert lib.hkv_page_visit_order(None, 0, 4, None, None) == H.OK
 
 
 def test_binding_validates_tensors_before_calling():

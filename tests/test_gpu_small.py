@@ -261,3 +261,37 @@ def test_side_stream_and_dm_zero_identity():
         kd, vd = O.dequant_records(ref, "fp8", 16, 8)
         check_values_exact(host_f64(ko)[0], O.round_output(kd[0], dt), f"{dt} K")
         check_values_exact(host_f64(vo)[0], O.round_output(vd[0], dt), f"{dt} V")
+
+
+def test_page_visit_order_and_fetch_invariance():
+    """The visiting order lists blocks by destination page, skipped blocks
+    last by index; fetching with it gives the same pages bit for bit."""
+    rng = np.random.default_rng(71)
+    for n, P in ((1, 1), (7, 9), (300, 300), (1024, 1024), (1500, 2000)):
+        table = rng.permutation(P)[:n].astype(np.int32)
+        if n > 5:
+            table[rng.choice(n, size=n // 5, replace=False)] = -1
+            table[rng.choice(n, size=n // 10, replace=False)] = P + 5
+        order = hkv.page_visit_order(_dev_i32(table), P).cpu().numpy()
+        live = (table >= 0) & (table < P)
+        want = np.concatenate([np.nonzero(live)[0][np.argsort(table[live], kind="stable")],
+                               np.nonzero(~live)[0]])
+        assert np.array_equal(order, want), (n, P)
+    w = W.GQA_REORDER
+    L, H = w.n_layers, w.n_kv_heads
+    kp = rng.standard_normal((L, w.n_blocks, 16, H, 128)).astype(np.float32)
+    vp = rng.standard_normal((L, w.n_blocks, 16, H, 128)).astype(np.float32)
+    table = np.arange(w.n_blocks, dtype=np.int32)
+    rec, ref, _ = _put_both(kp, vp, table, "fp8", "f32")
+    ftab = _dev_i32(rng.permutation(w.n_blocks))
+    dm = _dev_i32(rng.integers(-20000, 20000, size=w.n_blocks))
+    outs = []
+    for order in (None, hkv.page_visit_order(ftab, w.n_blocks),
+                  _dev_i32(rng.permutation(w.n_blocks))):
+        ko = torch.zeros((L, w.n_blocks, 16, H, 128), dtype=torch.bfloat16, device=DEV)
+        vo = torch.zeros_like(ko)
+        hkv.fetch_dequant_rope_shift(rec, "fp8", ftab, dm, 5e5, "half_split", ko, vo,
+                                     visit_order=order)
+        outs.append((ko.view(torch.int16).cpu(), vo.view(torch.int16).cpu()))
+    for k, v in outs[1:]:
+        assert torch.equal(k, outs[0][0]) and torch.equal(v, outs[0][1])

@@ -153,9 +153,13 @@ hipError_t launch_crc32(const Geometry& g, int64_t record_bytes, const RecordVie
   p.out = out;
   p.n_blocks = g.n_blocks;
   p.n_records = g.n_layers * g.n_blocks;
+  // Lane chunks are whole 128-byte cache lines when the record size allows
+  // (each batch of eight 16-byte loads then covers exactly one line), else
+  // 16-byte or 4-byte multiples; the difference is made up by leading zeros.
   const int64_t per_lane = (record_bytes + kWave - 1) / kWave;
   const bool aligned = record_bytes % 16 == 0;
-  const int64_t chunk = aligned ? (per_lane + 15) / 16 * 16 : (per_lane + 3) / 4 * 4;
+  const int64_t unit = record_bytes % 128 == 0 ? 128 : (aligned ? 16 : 4);
+  const int64_t chunk = (per_lane + unit - 1) / unit * unit;
   p.chunk = static_cast<int32_t>(chunk);
   p.pad = static_cast<int32_t>(kWave * chunk - record_bytes);
   p.aligned = aligned ? 1 : 0;

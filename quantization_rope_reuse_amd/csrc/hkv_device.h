@@ -180,13 +180,14 @@ __device__ __forceinline__ void int4x8_to_f32(uint32_t w, float (&x)[8]) {
 }
 
 // ---------------------------------------------------------------------------
-// Vector-wide max over the 8 lanes owning one vector.
+// Vector-wide max over the 8 lanes owning one vector, on magnitude bits
+// (non-negative finite floats order like their bit patterns).
 // ---------------------------------------------------------------------------
 
-__device__ __forceinline__ float max_over_vector_lanes(float v) {
-  v = fmaxf(v, __shfl_xor(v, 1, kLanesPerVec));
-  v = fmaxf(v, __shfl_xor(v, 2, kLanesPerVec));
-  v = fmaxf(v, __shfl_xor(v, 4, kLanesPerVec));
+__device__ __forceinline__ uint32_t max_bits_over_vector_lanes(uint32_t v) {
+  v = max(v, static_cast<uint32_t>(__shfl_xor(static_cast<int>(v), 1, kLanesPerVec)));
+  v = max(v, static_cast<uint32_t>(__shfl_xor(static_cast<int>(v), 2, kLanesPerVec)));
+  v = max(v, static_cast<uint32_t>(__shfl_xor(static_cast<int>(v), 4, kLanesPerVec)));
   return v;
 }
 

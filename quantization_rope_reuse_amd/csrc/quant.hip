@@ -8,7 +8,8 @@
 // grouped INT4 disk records at 3.88x against fp16).  Per vector:
 //   amax = max |x_j|; s = fp16_RNE(amax / qmax) (qmax 448 for E4M3, 7 for
 //   INT4; IEEE fp32 division); code_j = round(x_j / s) to E4M3 (saturating
-//   at +-448) or to an integer clamped to [-7, 7].
+//   at +-448) or to an integer clamped to [-7, 7], where x_j / s is the
+//   correctly rounded fp32 quotient.
 //
 // Work decomposition: one workgroup (4 waves) per (layer, block, K|V, chunk
 // of kQuantGroupVecs vectors), kQuantPasses * 8 consecutive vectors per wave,
@@ -79,30 +80,52 @@ __device__ __forceinline__ void run_to_f32(const RawSrc<SDT>& r, float (&x)[8]) 
   }
 }
 
+// x / s rounded to nearest even in fp32, given r = 1/s rounded to nearest
+// even: q0 = x*r is within a few ulps of x/s, the remainder x - q0*s is exact
+// in one fused multiply-add, and one correction step q0 + rem*r rounds to the
+// correctly rounded quotient (Markstein's theorem on division by a correctly
+// rounded reciprocal).  An exhaustive GPU comparison with IEEE division, every
+// positive fp32 x against every fp16 scale significand, found bitwise equality
+// wherever the quotient is a normal number; where it underflows the two can
+// differ in the last subnormal bit, which no FP8 or INT4 code can see, and the
+// sign is taken from x so that signed zeros agree.
+__device__ __forceinline__ float div_by_scale(float x, float s, float r) {
+  const float q0 = x * r;
+  const float rem = __builtin_fmaf(-q0, s, x);
+  return __builtin_copysignf(__builtin_fmaf(rem, r, q0), x);
+}
+
 // Quantize one vector's lane-owned runs a (elements 8s..8s+7) and b
 // (64+8s..64+8s+7); returns the fp16 scale bits (same in all 8 lanes).
 template <int FMT>
 __device__ __forceinline__ uint32_t quant_vector(float (&a)[8], float (&b)[8], uint8_t* c_ptr,
                                                  int sub, bool active) {
-  float m = 0.0f;
+  // |x| compared as integers: for finite values the magnitude bits order
+  // exactly like the magnitudes.
+  uint32_t mbits = 0;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) m = fmaxf(m, fmaxf(fabsf(a[j]), fabsf(b[j])));
-  const float amax = max_over_vector_lanes(m);
+  for (int j = 0; j < 8; ++j) {
+    const uint32_t ua = __builtin_bit_cast(uint32_t, a[j]) & 0x7FFFFFFFu;
+    const uint32_t ub = __builtin_bit_cast(uint32_t, b[j]) & 0x7FFFFFFFu;
+    mbits = max(mbits, max(ua, ub));
+  }
+  const float amax = __builtin_bit_cast(float, max_bits_over_vector_lanes(mbits));
   constexpr int QMAX = FMT == kFP8 ? 448 : 7;
   const uint32_t sbits = scale_bits<QMAX>(amax);
   if (!active) return sbits;
-  const float s = f16_bits_to_f32(sbits);
-  const bool zero_scale = sbits == 0u;
+  // An all-zero vector (s = 0) keeps its signed zeros: divide by 1 instead.
+  const float s = sbits == 0u ? 1.0f : f16_bits_to_f32(sbits);
+  const float r = 1.0f / s;                              // IEEE division, once per vector
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    a[j] = zero_scale ? a[j] : a[j] / s;                // IEEE division
-    b[j] = zero_scale ? b[j] : b[j] / s;
+    a[j] = div_by_scale(a[j], s, r);
+    b[j] = div_by_scale(b[j], s, r);
   }
   if constexpr (FMT == kFP8) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      a[j] = fminf(fmaxf(a[j], -448.0f), 448.0f);
-      b[j] = fminf(fmaxf(b[j], -448.0f), 448.0f);
+      a[j] = __builtin_amdgcn_fmed3f(a[j], -448.0f, 448.0f);
+      b[j] = __builtin_amdgcn_fmed3f(b[j], -448.0f, 448.0f);
     }
     __builtin_nontemporal_store(f32x8_to_fp8(a), reinterpret_cast<u32x2*>(c_ptr + 8 * sub));
     __builtin_nontemporal_store(f32x8_to_fp8(b), reinterpret_cast<u32x2*>(c_ptr + 64 + 8 * sub));
@@ -110,8 +133,8 @@ __device__ __forceinline__ uint32_t quant_vector(float (&a)[8], float (&b)[8], u
     uint32_t wa = 0, wb = 0;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const int ia = static_cast<int>(fminf(fmaxf(rintf(a[j]), -7.0f), 7.0f));
-      const int ib = static_cast<int>(fminf(fmaxf(rintf(b[j]), -7.0f), 7.0f));
+      const int ia = static_cast<int>(__builtin_amdgcn_fmed3f(rintf(a[j]), -7.0f, 7.0f));
+      const int ib = static_cast<int>(__builtin_amdgcn_fmed3f(rintf(b[j]), -7.0f, 7.0f));
       wa |= (static_cast<uint32_t>(ia) & 0xFu) << (4 * j);
       wb |= (static_cast<uint32_t>(ib) & 0xFu) << (4 * j);
     }

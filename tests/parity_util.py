@@ -41,18 +41,24 @@ def check_values_exact(gpu: np.ndarray, ref: np.ndarray, what: str):
 def check_keys(gpu: np.ndarray, exact: np.ndarray, deq: np.ndarray, dtype: str, what: str):
     """Rotated keys.  fp32 pages: |gpu - exact| <= 2e-6 * ||deq||_2 per
     vector (exact = the oracle's float64 result).  fp16 / bf16 pages: within
-    one unit in the last place of the oracle's rounded value."""
+    one unit in the last place of the oracle's rounded value, or within the
+    fp32 bound plus half a unit in the last place of the page dtype."""
     if dtype == "f32":
         err = np.max(np.abs(gpu - exact), axis=-1)
         bound = K_REL_TOL * np.sqrt(np.sum(deq * deq, axis=-1))
         worst = float(np.max(err / np.maximum(bound, 1e-300)))
         assert np.all(err <= bound), f"{what}: K error up to {worst:.3f} x bound"
         return worst
+    # A 16-bit page holds the fp32 result rounded once more, so a value also
+    # passes when it is within the fp32 bound plus half an ulp of the page
+    # dtype: near zero (cancellation inside a pair, fp16 subnormals) the fp32
+    # bound can exceed one ulp of the rounded oracle value.
     ref = O.round_output(exact, dtype)
     d = np.abs(gpu - ref)
-    ok = d <= ulp_of(ref, dtype)
+    bound = K_REL_TOL * np.sqrt(np.sum(deq * deq, axis=-1, keepdims=True))
+    ok = (d <= ulp_of(ref, dtype)) | (np.abs(gpu - exact) <= bound + ulp_of(gpu, dtype) / 2)
     n = int(np.count_nonzero(~ok))
-    assert n == 0, f"{what}: {n} K values beyond 1 ulp; e.g. gpu {gpu[~ok][:3]} oracle {ref[~ok][:3]}"
+    assert n == 0, f"{what}: {n} K values beyond tolerance; e.g. gpu {gpu[~ok][:3]} oracle {ref[~ok][:3]}"
     return float(np.max(d / ulp_of(ref, dtype)))
 
 

@@ -1,0 +1,201 @@
+"""GPU parity at the workloads' full sizes, in the launch configuration the
+benchmark uses: the Qwen3-8B-shaped cache (36 layers, 32k tokens, fp16, one
+call per operation), the Llama-3-70B-shaped cache (80 layers, 64k tokens,
+bf16, fetch layer by layer on a side stream) and the INT4 disk-tier cache
+(32 layers, 16k tokens, fp16 with outlier channels, CRC tamper test).
+
+The oracle cannot run over tens of gigabytes, so it runs on sampled blocks
+(seeded, plus the blocks with the extreme deltas and the first and last
+block): record bytes and CRC bit-exact, fetched values exact (V) or within one
+ulp (K).  Properties that hold at any size are checked over the whole cache
+with torch reductions: every destination page written, no NaN/Inf, value
+vectors within the FP8/INT4 error of their source and key vectors with their
+norm preserved."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from parity_util import (TORCH_OF, canary_fill, check_keys, check_values_exact, crc_u32,
+                         host_f64, is_canary)
+from quantization_rope_reuse_amd import hkv
+from quantization_rope_reuse_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def _fill_source(w, L=None):
+    """Source pages [L, P, T_b, H, 128] of the workload's dtype, logical block
+    b of each layer stored at page put_table[b]."""
+    L = L or w.n_layers
+    nb, tb, H = w.n_blocks, w.block_tokens, w.n_kv_heads
+    dt = TORCH_OF[w.src_dtype]
+    k = torch.empty((L, nb, tb, H, 128), dtype=dt, device=DEV)
+    v = torch.empty_like(k)
+    put_tab = torch.from_numpy(W.put_table(w)).to(DEV)
+    tmp = torch.empty((w.n_tokens, H, 128), dtype=torch.float32, device=DEV)
+    gen = torch.Generator(device=DEV)
+    for l in range(L):
+        for kv, dst in ((0, k), (1, v)):
+            W.device_layer_values(w, l, kv, tmp, generator=gen)
+            dst[l].index_copy_(0, put_tab.long(), tmp.view(nb, tb, H, 128).to(dt))
+    return k, v, put_tab
+
+
+def _samples(w, L, rng, n):
+    dm = W.delta_m(w)
+    blocks = {0, w.n_blocks - 1, int(np.argmax(dm)), int(np.argmin(dm))}
+    while len(blocks) < n:
+        blocks.add(int(rng.integers(w.n_blocks)))
+    layers = [0, L - 1] + [int(x) for x in rng.integers(0, L, size=n)]
+    return [(layers[i % len(layers)], b) for i, b in enumerate(sorted(blocks))]
+
+
+def _check_block(w, fmt, l, b, src_k, src_v, put_tab, rec, crc, out_k, out_v, ftab, dm):
+    """Oracle on one (layer, block) against the GPU's record, CRC and pages."""
+    page_src = int(put_tab[b])
+    xk = host_f64(src_k[l, page_src]).astype(np.float32)       # [T_b, H, 128]
+    xv = host_f64(src_v[l, page_src]).astype(np.float32)
+    quant = O.quant_fp8_vectors if fmt == "fp8" else O.quant_int4_vectors
+    kc, ks = quant(xk)
+    vc, vs = quant(xv)
+    ref = O.assemble_records(kc, vc, ks, vs)
+    got = rec[l, b].cpu().numpy()
+    assert np.array_equal(got, ref), f"layer {l} block {b}: {np.count_nonzero(got != ref)} bytes"
+    assert int(crc_u32(crc[l, b:b + 1])[0]) == int(O.crc32_records(ref[None])[0])
+    kd, vd = O.dequant_records(ref, fmt, w.block_tokens, w.n_kv_heads)
+    kr = O.rope_shift(kd, float(dm[b]), w.rope_base, w.pairs)
+    page = int(ftab[b])
+    kg = host_f64(out_k[l, page])
+    vg = host_f64(out_v[l, page])
+    check_values_exact(vg, O.round_output(vd, w.out_dtype), f"layer {l} block {b} V")
+    if dm[b] == 0:
+        check_values_exact(kg, O.round_output(kd, w.out_dtype), f"layer {l} block {b} K")
+    else:
+        check_keys(kg, kr, kd, w.out_dtype, f"layer {l} block {b} K")
+
+
+def _properties(src_k, src_v, put_tab, out_k, out_v, ftab, rel_v, rel_norm):
+    """Whole-cache properties, per layer to bound temporaries."""
+    inv = torch.argsort(ftab.long())
+    for l in range(src_k.shape[0]):
+        assert not bool(is_canary(out_k[l]).any()) and not bool(is_canary(out_v[l]).any())
+        ok = out_k[l].float()
+        ov = out_v[l].float()
+        assert bool(torch.isfinite(ok).all()) and bool(torch.isfinite(ov).all())
+        # the page holding logical block b is ftab[b]; the source page put_tab[b]
+        sk = src_k[l][put_tab.long()].float()
+        sv = src_v[l][put_tab.long()].float()
+        ok = ok[ftab.long()]
+        ov = ov[ftab.long()]
+        ev = (ov - sv).norm(dim=-1) / sv.norm(dim=-1).clamp_min(1e-30)
+        assert float(ev.max()) < rel_v, f"layer {l}: V relative error {float(ev.max()):.4f}"
+        en = (ok.norm(dim=-1) - sk.norm(dim=-1)).abs() / sk.norm(dim=-1).clamp_min(1e-30)
+        assert float(en.max()) < rel_norm, f"layer {l}: K norm change {float(en.max()):.4f}"
+        del ok, ov, sk, sv, ev, en
+    del inv
+
+
+@pytest.fixture(autouse=True)
+def _free_memory():
+    yield
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def test_qwen3_8b_full():
+    w = W.QWEN3_8B
+    print(f"[full] {w.name}", flush=True)
+    src_k, src_v, put_tab = _fill_source(w)
+    L, nb = w.n_layers, w.n_blocks
+    rec = hkv.alloc_records(L, nb, "fp8", w.block_tokens, w.n_kv_heads, device=DEV)
+    hkv.quant_fp8(src_k, src_v, put_tab, rec)
+    crc = hkv.crc32_blocks(rec, "fp8", w.block_tokens, w.n_kv_heads)
+    ftab = torch.from_numpy(W.fetch_table(w)).to(DEV)
+    dm_np = W.delta_m(w)
+    dm = torch.from_numpy(dm_np).to(DEV)
+    out_k = canary_fill(torch.empty_like(src_k))
+    out_v = canary_fill(torch.empty_like(src_v))
+    order = hkv.page_visit_order(ftab, nb)
+    hkv.fetch_dequant_rope_shift(rec, "fp8", ftab, dm, w.rope_base, w.pairs, out_k, out_v,
+                                 visit_order=order)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(81)
+    for l, b in _samples(w, L, rng, 8):
+        _check_block(w, "fp8", l, b, src_k, src_v, put_tab.cpu().numpy(), rec, crc, out_k,
+                     out_v, ftab.cpu().numpy(), dm_np)
+    _properties(src_k, src_v, put_tab, out_k, out_v, ftab, rel_v=0.08, rel_norm=0.08)
+
+
+def test_llama3_70b_full_layerwise_side_stream():
+    w = W.LLAMA3_70B
+    print(f"[full] {w.name}", flush=True)
+    src_k, src_v, put_tab = _fill_source(w)
+    L, nb = w.n_layers, w.n_blocks
+    rec = hkv.alloc_records(L, nb, "fp8", w.block_tokens, w.n_kv_heads, device=DEV)
+    hkv.quant_fp8(src_k, src_v, put_tab, rec)
+    crc = hkv.crc32_blocks(rec, "fp8", w.block_tokens, w.n_kv_heads)
+    ftab = torch.from_numpy(W.fetch_table(w)).to(DEV)
+    dm_np = W.delta_m(w)
+    dm = torch.from_numpy(dm_np).to(DEV)
+    out_k = canary_fill(torch.empty_like(src_k))
+    out_v = canary_fill(torch.empty_like(src_v))
+    side = torch.cuda.Stream()
+    ready = torch.cuda.Event()
+    ready.record(torch.cuda.current_stream())
+    side.wait_event(ready)
+    order = hkv.page_visit_order(ftab, nb, stream=side)
+    for l in range(L):
+        hkv.fetch_dequant_rope_shift(rec[l:l + 1], "fp8", ftab, dm, w.rope_base, w.pairs,
+                                     out_k[l:l + 1], out_v[l:l + 1], visit_order=order,
+                                     stream=side)
+    side.synchronize()
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(82)
+    for l, b in _samples(w, L, rng, 8):
+        _check_block(w, "fp8", l, b, src_k, src_v, put_tab.cpu().numpy(), rec, crc, out_k,
+                     out_v, ftab.cpu().numpy(), dm_np)
+    _properties(src_k, src_v, put_tab, out_k, out_v, ftab, rel_v=0.08, rel_norm=0.08)
+
+
+def test_int4_l3_full_with_tamper():
+    w = W.INT4_L3
+    print(f"[full] {w.name}", flush=True)
+    src_k, src_v, put_tab = _fill_source(w)
+    L, nb = w.n_layers, w.n_blocks
+    rec = hkv.alloc_records(L, nb, "int4", w.block_tokens, w.n_kv_heads, device=DEV)
+    hkv.quant_int4(src_k, src_v, put_tab, rec)
+    crc = hkv.crc32_blocks(rec, "int4", w.block_tokens, w.n_kv_heads)
+    ftab = torch.from_numpy(W.fetch_table(w)).to(DEV)
+    dm_np = W.delta_m(w)
+    dm = torch.from_numpy(dm_np).to(DEV)
+    out_k = canary_fill(torch.empty_like(src_k))
+    out_v = canary_fill(torch.empty_like(src_v))
+    hkv.fetch_dequant_rope_shift(rec, "int4", ftab, dm, w.rope_base, w.pairs, out_k, out_v)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(83)
+    for l, b in _samples(w, L, rng, 8):
+        _check_block(w, "int4", l, b, src_k, src_v, put_tab.cpu().numpy(), rec, crc, out_k,
+                     out_v, ftab.cpu().numpy(), dm_np)
+    # INT4 with outlier-dominated scales: a loose error bound, the parity above
+    # is the pass criterion
+    _properties(src_k, src_v, put_tab, out_k, out_v, ftab, rel_v=1.01, rel_norm=1.01)
+
+    # tamper detection: flip single bits / bytes in a few records; exactly
+    # those records' CRCs change, to the oracle's CRC of the tampered bytes
+    base_crc = crc_u32(crc)
+    for trial in range(4):
+        l, b = int(rng.integers(L)), int(rng.integers(nb))
+        j = int(rng.integers(rec.shape[2]))
+        mask = int(1 << rng.integers(8)) if trial % 2 == 0 else 0xFF
+        rec[l, b, j] ^= mask
+        new = crc_u32(hkv.crc32_blocks(rec, "int4", w.block_tokens, w.n_kv_heads))
+        diff = np.argwhere(new != base_crc)
+        assert diff.tolist() == [[l, b]], (trial, diff.tolist())
+        assert int(new[l, b]) == int(O.crc32_records(rec[l, b].cpu().numpy()[None])[0])
+        rec[l, b, j] ^= mask
+    again = crc_u32(hkv.crc32_blocks(rec, "int4", w.block_tokens, w.n_kv_heads))
+    assert np.array_equal(again, base_crc)

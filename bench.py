@@ -74,17 +74,24 @@ def source_digest(*names):
     return h.hexdigest()[:16]
 
 
-def measured_traffic(per_launch_alg_bytes):
+def measured_traffic():
     """HBM bytes per fetch launch from the committed rocprofv3 counter
-    summary, if it was taken on the current fetch source; else None."""
-    path = os.path.join(ROOT, "profiles", "fetch_llama3_70b_hbm_traffic.json")
+    summary, if it was taken on the current fetch sources; else None."""
+    path = os.path.join(ROOT, "profiles", "fetch_llama3_70b_hbm_traffic.txt")
     if not os.path.exists(path):
         return None
+    fields = {}
     with open(path) as f:
-        d = json.load(f)
-    if d.get("source_digest") != source_digest("fetch.hip", "hkv_device.h"):
+        for line in f:
+            if ":" in line and not line.startswith((" ", "|", "(")):
+                key, _, val = line.partition(":")
+                fields[key.strip()] = val.strip()
+    if fields.get("source_digest") != source_digest("fetch.hip", "hkv_device.h"):
         return None
-    return d.get("hbm_bytes_per_launch")
+    try:
+        return int(fields["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def main():
@@ -245,7 +252,7 @@ def main():
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": measured_traffic(fetch_launch_bytes),
+            "traffic": measured_traffic(),
             "alg_bytes_per_launch": fetch_launch_bytes,
             "mean_launch_ms": round(mean_fetch_ms, 5),
             "launch_ms_source": "HIP events on the fetch stream around the 80 per-layer "

@@ -4,50 +4,45 @@
 // permutation gives the fetch the same result; this one makes neighbouring
 // workgroups write neighbouring pages.
 //
-// Rank computation: thread b counts the blocks that sort before it, reading
-// the table through LDS tiles of 256 entries.  O(n^2) comparisons in total,
-// about 10 microseconds for a thousand blocks; meant for per-request tables of
-// up to a few thousand blocks.
+// Rank computation: one wave per block b reads the whole table with coalesced
+// loads, 64 entries per step, and counts the blocks that sort before b with
+// a wave ballot and a population count.  O(n^2) comparisons in total, spread
+// over n waves: a few microseconds for a thousand blocks; meant for
+// per-request tables of up to a few thousand blocks.
 #include "hkv_device.h"
 #include "hkv_launch.h"
 
 namespace hkv {
 namespace {
 
+constexpr int kBlocksPerGroup = kThreads / kWave;
+
 __global__ __launch_bounds__(kThreads) void page_order_kernel(const int32_t* table, int32_t n,
                                                              int32_t num_pages, int32_t* order) {
-  __shared__ int32_t tile[kThreads];
-  const int b = blockIdx.x * kThreads + threadIdx.x;
-  const int32_t mine = b < n ? table[b] : -1;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int b = blockIdx.x * kBlocksPerGroup + threadIdx.x / kWave;   // uniform per wave
+  if (b >= n) return;                                                 // whole wave
+  const int32_t mine = table[b];
   const bool live = mine >= 0 && mine < num_pages;
-  int32_t before = 0;     // blocks that sort before b
-  int32_t n_live = 0;     // live blocks in the whole table
-  for (int base = 0; base < n; base += kThreads) {
-    __syncthreads();
-    const int j = base + threadIdx.x;
-    tile[threadIdx.x] = j < n ? table[j] : -1;
-    __syncthreads();
-    const int cnt = min(kThreads, n - base);
-    for (int k = 0; k < cnt; ++k) {
-      const int32_t other = tile[k];
-      const int idx = base + k;
-      const bool other_live = other >= 0 && other < num_pages;
-      n_live += other_live ? 1 : 0;
-      if (live) {
-        before += (other_live && (other < mine || (other == mine && idx < b))) ? 1 : 0;
-      } else {
-        before += (!other_live && idx < b) ? 1 : 0;
-      }
-    }
+  uint32_t before = 0;     // blocks that sort before b
+  uint32_t n_live = 0;     // live blocks in the whole table
+  for (int base = 0; base < n; base += kWave) {
+    const int j = base + lane;
+    const int32_t other = j < n ? table[j] : -1;
+    const bool other_live = other >= 0 && other < num_pages;
+    const bool earlier = live ? (other_live && (other < mine || (other == mine && j < b)))
+                              : (j < n && !other_live && j < b);
+    before += __popcll(__ballot(earlier));
+    n_live += __popcll(__ballot(other_live));
   }
-  if (b < n) order[live ? before : n_live + before] = b;
+  if (lane == 0) order[live ? before : n_live + before] = b;
 }
 
 }  // namespace
 
 hipError_t launch_page_order(const int32_t* table, int32_t n_blocks, int32_t num_pages,
                              int32_t* order, hipStream_t stream) {
-  const unsigned groups = static_cast<unsigned>((n_blocks + kThreads - 1) / kThreads);
+  const unsigned groups = static_cast<unsigned>((n_blocks + kBlocksPerGroup - 1) / kBlocksPerGroup);
   hipLaunchKernelGGL(page_order_kernel, dim3(groups), dim3(kThreads), 0, stream, table, n_blocks,
                      num_pages, order);
   return hipGetLastError();

@@ -112,8 +112,9 @@ __global__ __launch_bounds__(kThreads) void fetch_kernel(FetchParams p) {
   const int slot = bk >> 1;
   const int blk = p.order ? p.order[slot] : slot;
   if (blk < 0 || blk >= p.n_blocks) return;
+  // The page is checked only after the code loads are issued, so its load
+  // latency overlaps theirs; the records of every listed block are readable.
   const int page = p.table[blk];
-  if (page < 0 || page >= p.num_pages) return;
 
   constexpr int CB = FMT == kFP8 ? kHeadDim : kHeadDim / 2;
   constexpr int ES = ElemSize<ODT>::value;
@@ -121,7 +122,6 @@ __global__ __launch_bounds__(kThreads) void fetch_kernel(FetchParams p) {
   const uint8_t* codes = rec + static_cast<int64_t>(kv) * p.vecs * CB;
   const uint16_t* scales =
       reinterpret_cast<const uint16_t*>(rec + 2LL * p.vecs * CB + 2LL * kv * p.vecs);
-  char* out = (kv ? p.v_out : p.k_out) + layer * p.o_layer + page * p.o_page;
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
@@ -142,6 +142,9 @@ __global__ __launch_bounds__(kThreads) void fetch_kernel(FetchParams p) {
     const int v = v0 + kVecsPerWave * i + vsub;
     if (v < v_end) raw[i] = load_codes<FMT>(codes, v, sub);
   }
+
+  if (page < 0 || page >= p.num_pages) return;   // skipped block: nothing stored
+  char* out = (kv ? p.v_out : p.k_out) + layer * p.o_layer + page * p.o_page;
 
   // Angle setup for keys with a nonzero delta (uniform per workgroup),
   // overlapping the loads above: lane i forms phi_i = dm * theta_i and its

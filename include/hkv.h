@@ -157,6 +157,21 @@ int hkv_fetch_dequant_rope_shift(const hkv_shape* shape, int32_t fmt,
                                  double rope_base, int32_t pairs, const hkv_pages* dst,
                                  int32_t dst_dtype, hipStream_t stream);
 
+/* Fetch with one delta per token: as hkv_fetch_dequant_rope_shift, but
+ * delta_m_tokens is an int32 [n_blocks][block_tokens] device array and each
+ * key vector is rotated by its own token's delta (for example -m to strip
+ * the cached positions' phase, as the KV-handoff module's strip_rope does,
+ * or a per-token re-layout).  phi = delta * theta_i and its reduction
+ * modulo pi/2 are computed in double (accurate for |phi| < 2^31); cos and sin
+ * of the reduced argument in fp32.  The tolerance is the same as for the
+ * per-block fetch. */
+int hkv_fetch_dequant_rope_shift_tokens(const hkv_shape* shape, int32_t fmt,
+                                        const hkv_records* src, const int32_t* block_table,
+                                        const int32_t* delta_m_tokens,
+                                        const int32_t* visit_order, double rope_base,
+                                        int32_t pairs, const hkv_pages* dst, int32_t dst_dtype,
+                                        hipStream_t stream);
+
 /* Visiting order for hkv_fetch_dequant_rope_shift: writes to order_out
  * (int32 [n_blocks], device) the logical blocks sorted by destination page
  * block_table[b]; blocks whose entry is negative or >= num_pages come last,

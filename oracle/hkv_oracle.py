@@ -450,9 +450,12 @@ def round_output(y, dtype):
 def fetch_exact(records, fmt, block_tokens, n_kv_heads, delta_m, base, pairs):
     """Unrounded fetch result per logical block: (K, V) float64
     [L, n_blocks, T_b, H, 128].  V is dequantized only; K is dequantized and
-    shifted by its block's delta_m."""
+    shifted by its delta: delta_m is [n_blocks] (one delta per block) or
+    [n_blocks, T_b] (one per token, e.g. -m to strip the cached phase as the
+    KV-handoff module's strip_rope does)."""
     kd, vd = dequant_records(records, fmt, block_tokens, n_kv_heads)
-    dm = np.asarray(delta_m, dtype=np.float64)[None, :, None, None]
+    dm = np.asarray(delta_m, dtype=np.float64)
+    dm = dm[None, :, None, None] if dm.ndim == 1 else dm[None, :, :, None]
     kr = rope_shift(kd, dm, base, pairs)
     return kr, vd
 

@@ -104,6 +104,27 @@ int quant_common(int32_t fmt, const hkv_shape* shape, const hkv_pages* src, int3
   return to_status(hkv::launch_quant(fmt, src_dtype, g, pv, block_table, rv, stream));
 }
 
+int fetch_common(const hkv_shape* shape, int32_t fmt, const hkv_records* src,
+                 const int32_t* block_table, const int32_t* delta_m, bool per_token,
+                 const int32_t* visit_order, double rope_base, int32_t pairs,
+                 const hkv_pages* dst, int32_t dst_dtype, hipStream_t stream) {
+  Geometry g;
+  PageView pv;
+  RecordView rv;
+  int st;
+  if (!valid_format(fmt)) return HKV_ERR_INVALID_ARG;
+  if ((st = check_shape(shape, &g)) != HKV_OK) return st;
+  if ((st = check_records(src, fmt, shape, &rv)) != HKV_OK) return st;
+  if ((st = check_pages(dst, dst_dtype, &pv)) != HKV_OK) return st;
+  if (pairs != HKV_ROPE_INTERLEAVED && pairs != HKV_ROPE_HALF_SPLIT) return HKV_ERR_INVALID_ARG;
+  if (!(rope_base > 0.0) || !isfinite(rope_base)) return HKV_ERR_INVALID_ARG;
+  if ((!block_table || !delta_m) && g.n_blocks > 0) return HKV_ERR_INVALID_ARG;
+  if (g.n_layers == 0 || g.n_blocks == 0) return HKV_OK;
+  return to_status(hkv::launch_fetch(fmt, dst_dtype, pairs, g, rv, block_table, delta_m,
+                                     per_token, visit_order, rope_base, pv, stream));
+}
+
+
 }  // namespace
 
 extern "C" {
@@ -136,24 +157,23 @@ int hkv_quant_int4(const hkv_shape* shape, const hkv_pages* src, int32_t src_dty
   return quant_common(HKV_INT4, shape, src, src_dtype, block_table, dst, stream);
 }
 
+
 int hkv_fetch_dequant_rope_shift(const hkv_shape* shape, int32_t fmt, const hkv_records* src,
                                  const int32_t* block_table, const int32_t* delta_m,
                                  const int32_t* visit_order, double rope_base, int32_t pairs,
                                  const hkv_pages* dst, int32_t dst_dtype, hipStream_t stream) {
-  Geometry g;
-  PageView pv;
-  RecordView rv;
-  int st;
-  if (!valid_format(fmt)) return HKV_ERR_INVALID_ARG;
-  if ((st = check_shape(shape, &g)) != HKV_OK) return st;
-  if ((st = check_records(src, fmt, shape, &rv)) != HKV_OK) return st;
-  if ((st = check_pages(dst, dst_dtype, &pv)) != HKV_OK) return st;
-  if (pairs != HKV_ROPE_INTERLEAVED && pairs != HKV_ROPE_HALF_SPLIT) return HKV_ERR_INVALID_ARG;
-  if (!(rope_base > 0.0) || !isfinite(rope_base)) return HKV_ERR_INVALID_ARG;
-  if ((!block_table || !delta_m) && g.n_blocks > 0) return HKV_ERR_INVALID_ARG;
-  if (g.n_layers == 0 || g.n_blocks == 0) return HKV_OK;
-  return to_status(hkv::launch_fetch(fmt, dst_dtype, pairs, g, rv, block_table, delta_m,
-                                     visit_order, rope_base, pv, stream));
+  return fetch_common(shape, fmt, src, block_table, delta_m, false, visit_order, rope_base,
+                      pairs, dst, dst_dtype, stream);
+}
+
+int hkv_fetch_dequant_rope_shift_tokens(const hkv_shape* shape, int32_t fmt,
+                                        const hkv_records* src, const int32_t* block_table,
+                                        const int32_t* delta_m_tokens,
+                                        const int32_t* visit_order, double rope_base,
+                                        int32_t pairs, const hkv_pages* dst, int32_t dst_dtype,
+                                        hipStream_t stream) {
+  return fetch_common(shape, fmt, src, block_table, delta_m_tokens, true, visit_order,
+                      rope_base, pairs, dst, dst_dtype, stream);
 }
 
 int hkv_page_visit_order(const int32_t* block_table, int32_t n_blocks, int32_t num_pages,

@@ -43,6 +43,7 @@ struct FetchParams {
   const int32_t* delta;
   const int32_t* order;      // optional visiting order of the blocks
   int32_t n_blocks;
+  int32_t block_tokens;
   char* k_out;
   char* v_out;
   int64_t o_layer, o_page, o_token, o_head;
@@ -97,13 +98,68 @@ __device__ __forceinline__ void rot(float& x, float& y, float c, float s) {
   y = ny;
 }
 
+// cos and sin of phi = dm * theta for per-token deltas: phi and its
+// reduction modulo pi/2 in double (pi/2 split into two doubles, so the
+// reduced argument is accurate to about 1e-16 for |phi| < 2^31), then fp32
+// sin / cos of the reduced argument (|r| <= pi/4) and the quadrant's signs.
+__device__ __forceinline__ void sincos_reduced(int dm, double theta, float* c, float* s) {
+  const double phi = static_cast<double>(dm) * theta;
+  const double k = rint(phi * 0.63661977236758134308);          // 2 / pi
+  double r = fma(-k, 1.5707963267948966192, phi);                // pi/2, high part
+  r = fma(-k, 6.1232339957367658e-17, r);                        // pi/2, low part
+  float sr, cr;
+  sincosf(static_cast<float>(r), &sr, &cr);
+  const int q = static_cast<int>(static_cast<int64_t>(k) & 3);
+  *c = q == 0 ? cr : (q == 1 ? -sr : (q == 2 ? -cr : sr));
+  *s = q == 0 ? sr : (q == 1 ? cr : (q == 2 ? -sr : -cr));
+}
+
+// Element-pair index of the j-th pair a lane rotates (see the lane layout in
+// hkv_device.h).
+template <int PAIRS>
+__device__ __forceinline__ int pair_of(int sub, int j) {
+  if constexpr (PAIRS == kInterleaved)
+    return j < 4 ? 4 * sub + j : 32 + 4 * sub + (j - 4);
+  else
+    return 8 * sub + j;
+}
+
+// (cos, sin) of the 8 pairs this lane rotates for vector v, per-token delta.
+// Called by every lane of the wave (the shared-token path exchanges values
+// across lanes); the token index is clamped so that lanes past the end of
+// the chunk read a valid delta whose result they then discard.
+template <int PAIRS>
+__device__ __forceinline__ void token_angles(const FetchParams& p, int blk, int v, int lane,
+                                             int sub, float (&cs)[8], float (&sn)[8]) {
+  const int t = min(v / p.n_heads, p.block_tokens - 1);
+  const int dm = p.delta[static_cast<int64_t>(blk) * p.block_tokens + t];
+  if (p.n_heads % kVecsPerWave == 0) {
+    // the pass's 8 vectors share one token: lane i computes pair i
+    float cf, sf;
+    sincos_reduced(dm, p.theta[lane], &cf, &sf);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      cs[j] = __shfl(cf, pair_of<PAIRS>(sub, j));
+      sn[j] = __shfl(sf, pair_of<PAIRS>(sub, j));
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) sincos_reduced(dm, p.theta[pair_of<PAIRS>(sub, j)], &cs[j], &sn[j]);
+  }
+}
+
 // Each wave owns kFetchPasses * 8 consecutive vectors of its workgroup's
 // chunk and moves them in kFetchPasses passes of 8.  All loads of the wave
 // are issued before its first store: one counter tracks a wave's loads and
 // stores in issue order, so a load issued after a store could not be waited
 // for without also waiting for that store.  Stores are non-temporal: the
 // pages are not read again by this kernel.
-template <int FMT, int ODT, int PAIRS>
+//
+// PER_TOKEN: delta is [n_blocks][block_tokens] and each key vector turns by
+// its own token's delta.  When the head count is a multiple of 8 the 8
+// vectors of a pass belong to one token and lane i computes pair i's angle
+// once per pass; otherwise each lane computes the 8 angles it needs.
+template <int FMT, int ODT, int PAIRS, bool PER_TOKEN>
 __global__ __launch_bounds__(kThreads) void fetch_kernel(FetchParams p) {
   const int layer = blockIdx.y;
   const int chunk = blockIdx.x % p.chunks;
@@ -146,10 +202,11 @@ __global__ __launch_bounds__(kThreads) void fetch_kernel(FetchParams p) {
   if (page < 0 || page >= p.num_pages) return;   // skipped block: nothing stored
   char* out = (kv ? p.v_out : p.k_out) + layer * p.o_layer + page * p.o_page;
 
-  // Angle setup for keys with a nonzero delta (uniform per workgroup),
-  // overlapping the loads above: lane i forms phi_i = dm * theta_i and its
-  // cos / sin in double precision (full range reduction), rounded to fp32.
-  const int dm = kv == 0 ? p.delta[blk] : 0;
+  // Per-block deltas: angle setup for keys with a nonzero delta (uniform per
+  // workgroup), overlapping the loads above: lane i forms phi_i = dm * theta_i
+  // and its cos / sin in double precision (full range reduction), rounded to
+  // fp32.
+  const int dm = (kv == 0 && !PER_TOKEN) ? p.delta[blk] : 0;
   const bool rotate = dm != 0;
   float cs[8], sn[8];
   if (rotate) {
@@ -159,13 +216,8 @@ __global__ __launch_bounds__(kThreads) void fetch_kernel(FetchParams p) {
     const float sf = static_cast<float>(sd);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      int idx;
-      if constexpr (PAIRS == kInterleaved)
-        idx = j < 4 ? 4 * sub + j : 32 + 4 * sub + (j - 4);
-      else
-        idx = 8 * sub + j;
-      cs[j] = __shfl(cf, idx);
-      sn[j] = __shfl(sf, idx);
+      cs[j] = __shfl(cf, pair_of<PAIRS>(sub, j));
+      sn[j] = __shfl(sf, pair_of<PAIRS>(sub, j));
     }
   }
 
@@ -173,10 +225,13 @@ __global__ __launch_bounds__(kThreads) void fetch_kernel(FetchParams p) {
   for (int i = 0; i < kFetchPasses; ++i) {
     const int v = v0 + kVecsPerWave * i + vsub;
     const float s = f16_bits_to_f32(__shfl(my_scale, kVecsPerWave * i + vsub));
+    if constexpr (PER_TOKEN) {
+      if (kv == 0) token_angles<PAIRS>(p, blk, v, lane, sub, cs, sn);   // all lanes
+    }
     if (v < v_end) {
       float a[8], b[8];
       dequant<FMT>(raw[i], s, a, b);
-      if (rotate) {
+      if (rotate || (PER_TOKEN && kv == 0)) {
         if constexpr (PAIRS == kInterleaved) {
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
@@ -197,36 +252,43 @@ __global__ __launch_bounds__(kThreads) void fetch_kernel(FetchParams p) {
   }
 }
 
-template <int FMT, int ODT, int PAIRS>
+template <int FMT, int ODT, int PAIRS, bool PT>
 hipError_t launch_t(const FetchParams& p, const Geometry& g, hipStream_t stream) {
   dim3 grid(static_cast<unsigned>(g.n_blocks) * 2u * static_cast<unsigned>(p.chunks),
             static_cast<unsigned>(g.n_layers));
-  hipLaunchKernelGGL((fetch_kernel<FMT, ODT, PAIRS>), grid, dim3(kThreads), 0, stream, p);
+  hipLaunchKernelGGL((fetch_kernel<FMT, ODT, PAIRS, PT>), grid, dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 
-template <int FMT, int ODT>
+template <int FMT, int ODT, bool PT>
 hipError_t launch_pairs(int pairs, const FetchParams& p, const Geometry& g, hipStream_t s) {
-  return pairs == kInterleaved ? launch_t<FMT, ODT, kInterleaved>(p, g, s)
-                               : launch_t<FMT, ODT, kHalfSplit>(p, g, s);
+  return pairs == kInterleaved ? launch_t<FMT, ODT, kInterleaved, PT>(p, g, s)
+                               : launch_t<FMT, ODT, kHalfSplit, PT>(p, g, s);
 }
 
-template <int FMT>
+template <int FMT, bool PT>
 hipError_t launch_dtype(int odt, int pairs, const FetchParams& p, const Geometry& g,
                         hipStream_t s) {
   switch (odt) {
-    case kF32: return launch_pairs<FMT, kF32>(pairs, p, g, s);
-    case kF16: return launch_pairs<FMT, kF16>(pairs, p, g, s);
-    default: return launch_pairs<FMT, kBF16>(pairs, p, g, s);
+    case kF32: return launch_pairs<FMT, kF32, PT>(pairs, p, g, s);
+    case kF16: return launch_pairs<FMT, kF16, PT>(pairs, p, g, s);
+    default: return launch_pairs<FMT, kBF16, PT>(pairs, p, g, s);
   }
+}
+
+template <bool PT>
+hipError_t launch_fmt(int fmt, int odt, int pairs, const FetchParams& p, const Geometry& g,
+                      hipStream_t s) {
+  return fmt == kFP8 ? launch_dtype<kFP8, PT>(odt, pairs, p, g, s)
+                     : launch_dtype<kINT4, PT>(odt, pairs, p, g, s);
 }
 
 }  // namespace
 
 hipError_t launch_fetch(int fmt, int dst_dtype, int pairs, const Geometry& g,
                         const RecordView& src, const int32_t* table, const int32_t* delta_m,
-                        const int32_t* visit_order, double rope_base, const PageView& dst,
-                        hipStream_t stream) {
+                        bool delta_per_token, const int32_t* visit_order, double rope_base,
+                        const PageView& dst, hipStream_t stream) {
   FetchParams p;
   p.rec = src.base;
   p.rec_layer = src.layer;
@@ -235,6 +297,7 @@ hipError_t launch_fetch(int fmt, int dst_dtype, int pairs, const Geometry& g,
   p.delta = delta_m;
   p.order = visit_order;
   p.n_blocks = g.n_blocks;
+  p.block_tokens = g.block_tokens;
   p.k_out = dst.k;
   p.v_out = dst.v;
   p.o_layer = dst.layer;
@@ -249,8 +312,8 @@ hipError_t launch_fetch(int fmt, int dst_dtype, int pairs, const Geometry& g,
   p.vecs_per_chunk = kFetchGroupVecs;
   for (int i = 0; i < kHeadDim / 2; ++i)
     p.theta[i] = 1.0 / pow(rope_base, static_cast<double>(2 * i) / kHeadDim);
-  return fmt == kFP8 ? launch_dtype<kFP8>(dst_dtype, pairs, p, g, stream)
-                     : launch_dtype<kINT4>(dst_dtype, pairs, p, g, stream);
+  return delta_per_token ? launch_fmt<true>(fmt, dst_dtype, pairs, p, g, stream)
+                         : launch_fmt<false>(fmt, dst_dtype, pairs, p, g, stream);
 }
 
 }  // namespace hkv

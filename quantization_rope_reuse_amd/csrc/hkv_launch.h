@@ -34,8 +34,8 @@ hipError_t launch_quant(int fmt, int src_dtype, const Geometry& g, const PageVie
 
 hipError_t launch_fetch(int fmt, int dst_dtype, int pairs, const Geometry& g,
                         const RecordView& src, const int32_t* table, const int32_t* delta_m,
-                        const int32_t* visit_order, double rope_base, const PageView& dst,
-                        hipStream_t stream);
+                        bool delta_per_token, const int32_t* visit_order, double rope_base,
+                        const PageView& dst, hipStream_t stream);
 
 hipError_t launch_page_order(const int32_t* table, int32_t n_blocks, int32_t num_pages,
                              int32_t* order, hipStream_t stream);

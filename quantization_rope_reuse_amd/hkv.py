@@ -82,10 +82,14 @@ def lib():
         l.hkv_fetch_dequant_rope_shift.argtypes = [
             P(Shape), ctypes.c_int32, P(Records), vp, vp, vp, ctypes.c_double, ctypes.c_int32,
             P(Pages), ctypes.c_int32, vp]
+        l.hkv_fetch_dequant_rope_shift_tokens.argtypes = [
+            P(Shape), ctypes.c_int32, P(Records), vp, vp, vp, ctypes.c_double, ctypes.c_int32,
+            P(Pages), ctypes.c_int32, vp]
         l.hkv_page_visit_order.argtypes = [vp, ctypes.c_int32, ctypes.c_int32, vp, vp]
         l.hkv_crc32_blocks.argtypes = [P(Shape), ctypes.c_int32, P(Records), vp, vp]
         for name in ("hkv_quant_fp8", "hkv_quant_int4", "hkv_fetch_dequant_rope_shift",
-                     "hkv_crc32_blocks", "hkv_page_visit_order"):
+                     "hkv_fetch_dequant_rope_shift_tokens", "hkv_crc32_blocks",
+                     "hkv_page_visit_order"):
             getattr(l, name).restype = ctypes.c_int
         l.hkv_record_bytes.argtypes = [ctypes.c_int32] * 4
         l.hkv_record_bytes.restype = ctypes.c_int64
@@ -192,27 +196,42 @@ def quant_int4(k_pages, v_pages, block_table, records, stream=None):
     return _quant("hkv_quant_int4", k_pages, v_pages, block_table, records, stream)
 
 
-def fetch_dequant_rope_shift(records, fmt, block_table, delta_m, rope_base, pairs,
-                             k_pages, v_pages, visit_order=None, stream=None):
-    """Dequantize records[:, b], shift keys by delta_m[b], store at page
-    block_table[b] of k/v_pages (dtype of the pages).  visit_order: optional
-    int32 permutation of the blocks (see page_visit_order)."""
+def _fetch(name, records, fmt, block_table, delta, n_delta, rope_base, pairs, k_pages, v_pages,
+           visit_order, stream):
     pages, shp, dt = _pages(k_pages, v_pages)
     L, _, tb, H, d = shp
     nb = block_table.numel()
-    if records.shape[0] != L or records.shape[1] != nb or delta_m.numel() != nb:
-        raise ValueError("records [L, n_blocks, bytes], table and delta_m must agree")
+    if records.shape[0] != L or records.shape[1] != nb or delta.numel() != n_delta(nb, tb):
+        raise ValueError("records [L, n_blocks, bytes], table and deltas must agree")
     if visit_order is not None and visit_order.numel() != nb:
         raise ValueError("visit_order must hold n_blocks entries")
     shape = Shape(L, nb, tb, H, d)
     rec = _records(records)
     order = None if visit_order is None else _i32(visit_order, "visit_order")
-    st = lib().hkv_fetch_dequant_rope_shift(
+    st = getattr(lib(), name)(
         ctypes.byref(shape), FORMATS[fmt], ctypes.byref(rec), _i32(block_table, "block_table"),
-        _i32(delta_m, "delta_m"), order, float(rope_base), PAIRS[pairs], ctypes.byref(pages),
+        _i32(delta, "delta_m"), order, float(rope_base), PAIRS[pairs], ctypes.byref(pages),
         dt, _stream(stream, k_pages.device))
-    _check("hkv_fetch_dequant_rope_shift", st)
+    _check(name, st)
     return k_pages, v_pages
+
+
+def fetch_dequant_rope_shift(records, fmt, block_table, delta_m, rope_base, pairs,
+                             k_pages, v_pages, visit_order=None, stream=None):
+    """Dequantize records[:, b], shift keys by delta_m[b], store at page
+    block_table[b] of k/v_pages (dtype of the pages).  visit_order: optional
+    int32 permutation of the blocks (see page_visit_order)."""
+    return _fetch("hkv_fetch_dequant_rope_shift", records, fmt, block_table, delta_m,
+                  lambda nb, tb: nb, rope_base, pairs, k_pages, v_pages, visit_order, stream)
+
+
+def fetch_dequant_rope_shift_tokens(records, fmt, block_table, delta_m_tokens, rope_base, pairs,
+                                    k_pages, v_pages, visit_order=None, stream=None):
+    """As fetch_dequant_rope_shift with one delta per token: delta_m_tokens
+    is an int32 [n_blocks, block_tokens] tensor."""
+    return _fetch("hkv_fetch_dequant_rope_shift_tokens", records, fmt, block_table,
+                  delta_m_tokens, lambda nb, tb: nb * tb, rope_base, pairs, k_pages, v_pages,
+                  visit_order, stream)
 
 
 def page_visit_order(block_table, num_pages: int, out=None, stream=None):

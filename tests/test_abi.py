@@ -14,7 +14,7 @@ def test_exports_every_declared_symbol():
     names = H.declared_symbols()
     assert set(names) == {"hkv_quant_fp8", "hkv_quant_int4", "hkv_fetch_dequant_rope_shift",
                           "hkv_crc32_blocks", "hkv_record_bytes", "hkv_status_string",
-                          "hkv_page_visit_order"}
+                          "hkv_page_visit_order", "hkv_fetch_dequant_rope_shift_tokens"}
     lib = H.lib()
     for n in names:
         assert getattr(lib, n) is not None
@@ -132,6 +132,20 @@ def test_fetch_rejects_bad_arguments(name, kw):
     st = _fetch(_shape(), _recs(), a["table"], a["dm"], a["base"], a["pairs"], _pages(),
                 a["dtype"], a["fmt"])
     assert st == H.ERR_INVALID_ARG
+
+
+def test_fetch_tokens_rejects_bad_arguments():
+    lib = H.lib()
+    s, r, p = _shape(), _recs(), _pages()
+    call = lambda **kw: lib.hkv_fetch_dequant_rope_shift_tokens(
+        ctypes.byref(s), kw.get("fmt", 0), ctypes.byref(r), ctypes.c_void_p(kw.get("t", FAKE)),
+        ctypes.c_void_p(kw.get("dm", FAKE)), None, kw.get("base", 1e4), kw.get("pairs", 0),
+        ctypes.byref(p), kw.get("dt", 0), None)
+    assert call(dm=0) == H.ERR_INVALID_ARG
+    assert call(t=0) == H.ERR_INVALID_ARG
+    assert call(base=-1.0) == H.ERR_INVALID_ARG
+    assert call(pairs=5) == H.ERR_INVALID_ARG
+    assert call(fmt=3) == H.ERR_INVALID_ARG
 
 
 def test_crc_rejects_bad_arguments():

@@ -295,3 +295,57 @@ def test_page_visit_order_and_fetch_invariance():
         outs.append((ko.view(torch.int16).cpu(), vo.view(torch.int16).cpu()))
     for k, v in outs[1:]:
         assert torch.equal(k, outs[0][0]) and torch.equal(v, outs[0][1])
+
+
+@pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
+def test_per_token_strip_rope(out_dtype):
+    """One delta per token, -m_old: the fetched keys are the stripped keys
+    (the tiny workload's pre-RoPE keys up to the FP8 error), against the
+    oracle's per-token shift."""
+    w, kp, vp, table = _tiny_inputs()
+    rec, ref, _ = _put_both(kp, vp, table, "fp8", "f32")
+    pos = W.tiny_positions().reshape(4, 16)
+    dmt = (-pos).astype(np.int32)
+    tdt = TORCH_OF[out_dtype]
+    ko = canary_fill(torch.empty((1, 4, 16, 8, 128), dtype=tdt, device=DEV))
+    vo = canary_fill(torch.empty_like(ko))
+    hkv.fetch_dequant_rope_shift_tokens(rec, "fp8", _dev_i32(table), _dev_i32(dmt), w.rope_base,
+                                        w.pairs, ko, vo)
+    torch.cuda.synchronize()
+    kr, vd = O.fetch_exact(ref, "fp8", 16, 8, dmt, w.rope_base, w.pairs)
+    kd, _ = O.dequant_records(ref, "fp8", 16, 8)
+    kg, vg = host_f64(ko), host_f64(vo)
+    check_values_exact(vg[0], O.round_output(vd[0], out_dtype), "V")
+    check_keys(kg[0], kr[0], kd[0], out_dtype, "K stripped")
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "int4"])
+@pytest.mark.parametrize("tb,H", [(16, 8), (7, 3), (5, 16)])
+def test_per_token_random_and_extreme_deltas(fmt, tb, H):
+    """Random per-token deltas including 0 and values near +-2^31 (range
+    reduction of phi up to 2e9 rad), head counts that share a token across a
+    pass (8, 16) and that do not (3)."""
+    rng = np.random.default_rng(91)
+    L, P = 2, 5
+    kp = rng.standard_normal((L, P, tb, H, 128)).astype(np.float32)
+    vp = rng.standard_normal((L, P, tb, H, 128)).astype(np.float32)
+    table = rng.permutation(P).astype(np.int32)
+    rec, ref, _ = _put_both(kp, vp, table, fmt, "f32")
+    dmt = rng.integers(-40000, 40000, size=(P, tb)).astype(np.int64)
+    dmt[0, 0] = 0
+    dmt[1, :2] = [2 ** 31 - 1, -(2 ** 31)]
+    dmt[2, 0] = 1 << 30
+    dmt = dmt.astype(np.int32)
+    ftab = rng.permutation(P).astype(np.int32)
+    for base, pairs in ((1e4, "interleaved"), (5e5, "half_split")):
+        ko = canary_fill(torch.empty((L, P, tb, H, 128), dtype=torch.float32, device=DEV))
+        vo = canary_fill(torch.empty_like(ko))
+        hkv.fetch_dequant_rope_shift_tokens(rec, fmt, _dev_i32(ftab), _dev_i32(dmt), base,
+                                            pairs, ko, vo)
+        torch.cuda.synchronize()
+        kr, vd = O.fetch_exact(ref, fmt, tb, H, dmt, base, pairs)
+        kd, _ = O.dequant_records(ref, fmt, tb, H)
+        kg, vg = host_f64(ko), host_f64(vo)
+        for b, page in enumerate(ftab):
+            check_values_exact(vg[:, page], O.round_output(vd[:, b], "f32"), f"V block {b}")
+            check_keys(kg[:, page], kr[:, b], kd[:, b], "f32", f"K block {b} {pairs}")

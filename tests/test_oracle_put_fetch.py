@@ -92,3 +92,24 @@ def test_output_rounding_is_rne_of_fp32():
     assert bf[4] < 0 and abs(bf[4] / -1e-30 - 1) < 2 ** -8
     f16 = O.round_output(y, "f16")
     assert f16[2] == 1.0 and np.isinf(f16[3]) and f16[4] == 0.0 and np.signbit(f16[4])
+
+
+def test_per_token_deltas():
+    """One delta per token: constant per-token deltas equal the per-block
+    fetch; deltas of -m_old strip the cached phase (RoPE of the dequantized
+    pre-RoPE keys at position 0 is the identity)."""
+    w, k_post, v, rec = _tiny_records()
+    dm = W.delta_m(w)
+    per_block = O.fetch_exact(rec, O.FMT_FP8, 16, 8, dm, w.rope_base, w.pairs)
+    per_token = O.fetch_exact(rec, O.FMT_FP8, 16, 8, np.repeat(dm[:, None], 16, axis=1),
+                              w.rope_base, w.pairs)
+    assert np.array_equal(per_block[0], per_token[0])
+    pos = W.tiny_positions().reshape(4, 16)
+    kr, _ = O.fetch_exact(rec, O.FMT_FP8, 16, 8, -pos, w.rope_base, w.pairs)
+    kd, _ = O.dequant_records(rec, O.FMT_FP8, 16, 8)
+    want = O.rope_strip(kd[0].reshape(64, 8, 128), pos.ravel(), w.rope_base, w.pairs)
+    assert np.max(np.abs(kr[0].reshape(64, 8, 128) - want)) < 1e-12
+    # the stripped keys are the pre-RoPE keys up to the FP8 error
+    k_pre, _ = W.tiny_pre_rope_kv()
+    rel = np.linalg.norm(kr[0].reshape(64, 8, 128) - k_pre) / np.linalg.norm(k_pre)
+    assert rel < 0.05

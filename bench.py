@@ -60,6 +60,11 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--layers", type=int, default=None,
                    help="override the layer count (profiling runs only)")
+    p.add_argument("--overlap", action="store_true",
+                   help="instead of the metric line, measure the layer-wise overlap of the "
+                        "fetch with a synthetic suffix compute (bf16 GEMM per layer)")
+    p.add_argument("--suffix-tokens", type=int, default=512,
+                   help="suffix tokens of the synthetic per-layer compute (--overlap)")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="also run a plain 1 GiB read + 1 GiB write elementwise kernel "
                         "(reference for scaling HBM byte counters)")
@@ -211,6 +216,24 @@ def main():
     if bool(torch.isnan(out_k).any()) or bool(torch.isnan(out_v).any()):
         raise RuntimeError("fetch produced NaN")
 
+    # per-token deltas (the same +8192 for every token), 80 launches, timed once
+    dm_tok = dm.view(nb, 1).expand(nb, tb).contiguous()
+    ev_t = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    for rep in range(2):
+        ev_t[0].record(side)
+        for l in range(L):
+            hkv.fetch_dequant_rope_shift_tokens(rec_l[l], "fp8", ftab, dm_tok, w.rope_base,
+                                                w.pairs, ok_l[l], ov_l[l], visit_order=order,
+                                                stream=side)
+        ev_t[1].record(side)
+        side.synchronize()
+    tok_ms = ev_t[0].elapsed_time(ev_t[1])
+
+    if a.overlap:
+        print(json.dumps(overlap(a, w, L, hkv, rec_l, ok_l, ov_l, ftab, dm, order, side)),
+              flush=True)
+        return
+
     if a.calibrate_copy:
         # torch.neg over 2**28 fp32 values: reads exactly 1 GiB, writes 1 GiB
         del src_k, src_v, out_k, out_v, records
@@ -265,6 +288,11 @@ def main():
             "tokens_per_s": round(tokens_per_s, 0),
             "ms_80_layers": round(float(np.mean(fetch_span_ms)), 4),
         },
+        "fetch_per_token_delta": {
+            "gbps": round(fetch_bytes / (tok_ms * 1e-3) / 1e9, 1),
+            "ms_80_layers": round(tok_ms, 4),
+            "note": "hkv_fetch_dequant_rope_shift_tokens, one delta per token",
+        },
         "put": {"mean_ms": round(float(np.mean(put_ms)), 4),
                 "gbps": round(put_bytes / (float(np.mean(put_ms)) * 1e-3) / 1e9, 1)},
         "crc32": {"mean_ms_incl_stream_handoff": round(float(np.mean(crc_ms)), 4),
@@ -272,6 +300,73 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
+
+
+def overlap(a, w, L, hkv, rec_l, ok_l, ov_l, ftab, dm, order, side):
+    """Layer-wise overlap (the HyperCache post's layer-wise transfer
+    paragraph): the fetch of layer l+1 runs on a side stream while the main
+    stream runs layer l's suffix compute, which needs layer l's fetched KV.
+    The suffix compute is a synthetic bf16 GEMM with the FLOPs of one
+    Llama-3-70B layer over `suffix_tokens` tokens (2 * S * 70e9 / 80)."""
+    import torch
+
+    dev = rec_l[0].device
+    main = torch.cuda.current_stream(dev)
+    S = a.suffix_tokens
+    x = torch.randn((S, 8192), dtype=torch.bfloat16, device=dev)
+    wt = torch.randn((8192, 106496), dtype=torch.bfloat16, device=dev) * 0.01
+    y = torch.empty((S, 106496), dtype=torch.bfloat16, device=dev)
+
+    def compute():
+        torch.matmul(x, wt, out=y)
+
+    def fetch(l):
+        hkv.fetch_dequant_rope_shift(rec_l[l], "fp8", ftab, dm, w.rope_base, w.pairs,
+                                     ok_l[l], ov_l[l], visit_order=order, stream=side)
+
+    def timed(fn, reps=3):
+        best = None
+        for _ in range(reps):
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            fn()
+            torch.cuda.synchronize()
+            dt = (time.perf_counter() - t0) * 1e3
+            best = dt if best is None else min(best, dt)
+        return best
+
+    def compute_only():
+        for _ in range(L):
+            compute()
+
+    def fetch_only():
+        with torch.cuda.stream(side):
+            for l in range(L):
+                fetch(l)
+
+    def overlapped():
+        done = [torch.cuda.Event() for _ in range(L)]
+        start = torch.cuda.Event()
+        start.record(main)
+        side.wait_event(start)
+        for l in range(L):               # the side stream runs ahead, layer by layer
+            fetch(l)
+            done[l].record(side)
+        for l in range(L):
+            main.wait_event(done[l])     # layer l's compute needs layer l's KV
+            compute()
+
+    timed(compute_only, 1)
+    c = timed(compute_only)
+    f = timed(fetch_only)
+    o = timed(overlapped)
+    return {
+        "mode": "layer-wise overlap", "layers": L, "suffix_tokens": S,
+        "gemm": f"[{S} x 8192] @ [8192 x 106496] bf16 per layer (torch.matmul)",
+        "compute_only_ms": round(c, 3), "fetch_only_ms": round(f, 3),
+        "overlapped_ms": round(o, 3), "exposed_fetch_ms": round(o - c, 3),
+        "hidden_fraction_of_fetch": round(1.0 - max(0.0, o - c) / f, 4),
+    }
 
 
 def cpu_baseline(w, records_bytes, budget_s):

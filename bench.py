@@ -65,6 +65,9 @@ def parse():
                         "fetch with a synthetic suffix compute (bf16 GEMM per layer)")
     p.add_argument("--suffix-tokens", type=int, default=512,
                    help="suffix tokens of the synthetic per-layer compute (--overlap)")
+    p.add_argument("--fetch-cus", type=int, nargs="*", default=[16, 32],
+                   help="compute units given to the fetch stream in the CU-partitioned "
+                        "overlap runs (--overlap)")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="also run a plain 1 GiB read + 1 GiB write elementwise kernel "
                         "(reference for scaling HBM byte counters)")
@@ -307,22 +310,16 @@ def overlap(a, w, L, hkv, rec_l, ok_l, ov_l, ftab, dm, order, side):
     paragraph): the fetch of layer l+1 runs on a side stream while the main
     stream runs layer l's suffix compute, which needs layer l's fetched KV.
     The suffix compute is a synthetic bf16 GEMM with the FLOPs of one
-    Llama-3-70B layer over `suffix_tokens` tokens (2 * S * 70e9 / 80)."""
+    Llama-3-70B layer over `suffix_tokens` tokens (2 * S * 70e9 / 80).
+    Measured twice: with two ordinary streams (the GEMM may hold every CU),
+    and with hkv_stream_pair_create's CU-partitioned streams."""
     import torch
 
     dev = rec_l[0].device
-    main = torch.cuda.current_stream(dev)
     S = a.suffix_tokens
     x = torch.randn((S, 8192), dtype=torch.bfloat16, device=dev)
     wt = torch.randn((8192, 106496), dtype=torch.bfloat16, device=dev) * 0.01
     y = torch.empty((S, 106496), dtype=torch.bfloat16, device=dev)
-
-    def compute():
-        torch.matmul(x, wt, out=y)
-
-    def fetch(l):
-        hkv.fetch_dequant_rope_shift(rec_l[l], "fp8", ftab, dm, w.rope_base, w.pairs,
-                                     ok_l[l], ov_l[l], visit_order=order, stream=side)
 
     def timed(fn, reps=3):
         best = None
@@ -335,38 +332,51 @@ def overlap(a, w, L, hkv, rec_l, ok_l, ov_l, ftab, dm, order, side):
             best = dt if best is None else min(best, dt)
         return best
 
-    def compute_only():
-        for _ in range(L):
-            compute()
+    def run(fetch_stream, compute_stream):
+        def fetch(l):
+            hkv.fetch_dequant_rope_shift(rec_l[l], "fp8", ftab, dm, w.rope_base, w.pairs,
+                                         ok_l[l], ov_l[l], visit_order=order,
+                                         stream=fetch_stream)
 
-    def fetch_only():
-        with torch.cuda.stream(side):
+        def compute_only():
+            with torch.cuda.stream(compute_stream):
+                for _ in range(L):
+                    torch.matmul(x, wt, out=y)
+
+        def fetch_only():
             for l in range(L):
                 fetch(l)
 
-    def overlapped():
-        done = [torch.cuda.Event() for _ in range(L)]
-        start = torch.cuda.Event()
-        start.record(main)
-        side.wait_event(start)
-        for l in range(L):               # the side stream runs ahead, layer by layer
-            fetch(l)
-            done[l].record(side)
-        for l in range(L):
-            main.wait_event(done[l])     # layer l's compute needs layer l's KV
-            compute()
+        def overlapped():
+            done = [torch.cuda.Event() for _ in range(L)]
+            start = torch.cuda.Event()
+            start.record(torch.cuda.current_stream(dev))
+            fetch_stream.wait_event(start)
+            compute_stream.wait_event(start)
+            for l in range(L):            # the fetch stream runs ahead, layer by layer
+                fetch(l)
+                done[l].record(fetch_stream)
+            with torch.cuda.stream(compute_stream):
+                for l in range(L):
+                    compute_stream.wait_event(done[l])   # layer l needs its KV
+                    torch.matmul(x, wt, out=y)
 
-    timed(compute_only, 1)
-    c = timed(compute_only)
-    f = timed(fetch_only)
-    o = timed(overlapped)
-    return {
-        "mode": "layer-wise overlap", "layers": L, "suffix_tokens": S,
-        "gemm": f"[{S} x 8192] @ [8192 x 106496] bf16 per layer (torch.matmul)",
-        "compute_only_ms": round(c, 3), "fetch_only_ms": round(f, 3),
-        "overlapped_ms": round(o, 3), "exposed_fetch_ms": round(o - c, 3),
-        "hidden_fraction_of_fetch": round(1.0 - max(0.0, o - c) / f, 4),
-    }
+        timed(compute_only, 1)
+        c, f, o = timed(compute_only), timed(fetch_only), timed(overlapped)
+        return {"compute_only_ms": round(c, 3), "fetch_only_ms": round(f, 3),
+                "overlapped_ms": round(o, 3), "exposed_fetch_ms": round(o - c, 3),
+                "hidden_fraction_of_fetch": round(1.0 - max(0.0, o - c) / f, 4)}
+
+    out = {"mode": "layer-wise overlap", "layers": L, "suffix_tokens": S,
+           "gemm": f"[{S} x 8192] @ [8192 x 106496] bf16 per layer (torch.matmul)",
+           "ordinary_streams": run(side, torch.cuda.Stream(device=dev))}
+    for n in a.fetch_cus:
+        pair = hkv.StreamPair(n, device=dev)
+        try:
+            out[f"cu_partition_{n}"] = run(pair.fetch, pair.compute)
+        finally:
+            pair.close()
+    return out
 
 
 def cpu_baseline(w, records_bytes, budget_s):

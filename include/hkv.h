@@ -189,6 +189,17 @@ int hkv_page_visit_order(const int32_t* block_table, int32_t n_blocks, int32_t n
 int hkv_crc32_blocks(const hkv_shape* shape, int32_t fmt, const hkv_records* src,
                      uint32_t* crc_out, hipStream_t stream);
 
+/* Layer-wise overlap (HyperCache post, Core Design, layer-wise transfer
+ * paragraph: layer l+1 is fetched while layer l computes).  Creates two
+ * streams on the current device that split its compute units: the first
+ * fetch_cus of them for *fetch_stream, all others for *compute_stream.  Kernels on the two streams then run side by side
+ * instead of the fetch waiting for gaps in a compute kernel that holds every
+ * CU.  Both streams have the default priority; release them with
+ * hkv_stream_destroy.  HKV_ERR_INVALID_ARG unless 1 <= fetch_cus < CU count. */
+int hkv_stream_pair_create(int32_t fetch_cus, hipStream_t* fetch_stream,
+                           hipStream_t* compute_stream);
+int hkv_stream_destroy(hipStream_t stream);
+
 /* Host-only helpers. */
 
 /* Bytes of one record: 2*N*C + 4*N (see hkv_records); -1 on bad arguments. */

@@ -87,6 +87,10 @@ def lib():
             P(Pages), ctypes.c_int32, vp]
         l.hkv_page_visit_order.argtypes = [vp, ctypes.c_int32, ctypes.c_int32, vp, vp]
         l.hkv_crc32_blocks.argtypes = [P(Shape), ctypes.c_int32, P(Records), vp, vp]
+        l.hkv_stream_pair_create.argtypes = [ctypes.c_int32, P(vp), P(vp)]
+        l.hkv_stream_pair_create.restype = ctypes.c_int
+        l.hkv_stream_destroy.argtypes = [vp]
+        l.hkv_stream_destroy.restype = ctypes.c_int
         for name in ("hkv_quant_fp8", "hkv_quant_int4", "hkv_fetch_dequant_rope_shift",
                      "hkv_fetch_dequant_rope_shift_tokens", "hkv_crc32_blocks",
                      "hkv_page_visit_order"):
@@ -246,6 +250,26 @@ def page_visit_order(block_table, num_pages: int, out=None, stream=None):
                                     _i32(out, "out"), _stream(stream, block_table.device))
     _check("hkv_page_visit_order", st)
     return out
+
+
+class StreamPair:
+    """Two CU-partitioned streams (hkv_stream_pair_create) as torch streams:
+    `fetch` with fetch_cus compute units, `compute` with the rest."""
+
+    def __init__(self, fetch_cus: int, device=None):
+        f, c = ctypes.c_void_p(), ctypes.c_void_p()
+        _check("hkv_stream_pair_create",
+               lib().hkv_stream_pair_create(int(fetch_cus), ctypes.byref(f), ctypes.byref(c)))
+        self._handles = (f.value, c.value)
+        self.fetch = torch.cuda.ExternalStream(f.value, device=device)
+        self.compute = torch.cuda.ExternalStream(c.value, device=device)
+
+    def close(self):
+        if self._handles:
+            torch.cuda.synchronize()
+            for h in self._handles:
+                lib().hkv_stream_destroy(ctypes.c_void_p(h))
+            self._handles = None
 
 
 def crc32_blocks(records, fmt, block_tokens: int, n_kv_heads: int, out=None, stream=None):

@@ -14,7 +14,8 @@ def test_exports_every_declared_symbol():
     names = H.declared_symbols()
     assert set(names) == {"hkv_quant_fp8", "hkv_quant_int4", "hkv_fetch_dequant_rope_shift",
                           "hkv_crc32_blocks", "hkv_record_bytes", "hkv_status_string",
-                          "hkv_page_visit_order", "hkv_fetch_dequant_rope_shift_tokens"}
+                          "hkv_page_visit_order", "hkv_fetch_dequant_rope_shift_tokens",
+                          "hkv_stream_pair_create", "hkv_stream_destroy"}
     lib = H.lib()
     for n in names:
         assert getattr(lib, n) is not None
@@ -146,6 +147,14 @@ def test_fetch_tokens_rejects_bad_arguments():
     assert call(base=-1.0) == H.ERR_INVALID_ARG
     assert call(pairs=5) == H.ERR_INVALID_ARG
     assert call(fmt=3) == H.ERR_INVALID_ARG
+
+
+def test_stream_helpers_reject_null_arguments():
+    lib = H.lib()
+    p = ctypes.c_void_p()
+    assert lib.hkv_stream_pair_create(8, None, ctypes.byref(p)) == H.ERR_INVALID_ARG
+    assert lib.hkv_stream_pair_create(8, ctypes.byref(p), None) == H.ERR_INVALID_ARG
+    assert lib.hkv_stream_destroy(None) == H.ERR_INVALID_ARG
 
 
 def test_crc_rejects_bad_arguments():

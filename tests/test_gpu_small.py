@@ -349,3 +349,30 @@ def test_per_token_random_and_extreme_deltas(fmt, tb, H):
         for b, page in enumerate(ftab):
             check_values_exact(vg[:, page], O.round_output(vd[:, b], "f32"), f"V block {b}")
             check_keys(kg[:, page], kr[:, b], kd[:, b], "f32", f"K block {b} {pairs}")
+
+
+def test_cu_partitioned_stream_pair():
+    """A fetch on each stream of hkv_stream_pair_create gives the same pages
+    as on the default stream."""
+    w, kp, vp, table = _tiny_inputs()
+    rec, ref, _ = _put_both(kp, vp, table, "fp8", "f32")
+    dm = _dev_i32(W.delta_m(w))
+    tab = _dev_i32(table)
+    outs = []
+    pair = hkv.StreamPair(8)
+    try:
+        for stream in (None, pair.fetch, pair.compute):
+            ko = torch.zeros((1, 4, 16, 8, 128), dtype=torch.float32, device=DEV)
+            vo = torch.zeros_like(ko)
+            torch.cuda.synchronize()
+            hkv.fetch_dequant_rope_shift(rec, "fp8", tab, dm, w.rope_base, w.pairs, ko, vo,
+                                         stream=stream)
+            torch.cuda.synchronize()
+            outs.append((ko.cpu(), vo.cpu()))
+    finally:
+        pair.close()
+    for k, v in outs[1:]:
+        assert torch.equal(k.view(torch.int32), outs[0][0].view(torch.int32))
+        assert torch.equal(v.view(torch.int32), outs[0][1].view(torch.int32))
+    with pytest.raises(hkv.HkvError):
+        hkv.StreamPair(100000)

@@ -26,6 +26,9 @@ Sources (web pages; cited by title and section):
     - The module13.py listing, functions rope_cache / apply_rope /
       strip_rope: the angle table theta_i = 1 / base**(2i/d), the pair
       rotation and its sign convention, and the inverse rotation.
+* The HyperCache post again, Core Design, recompute paragraph, and the
+  "15% CacheBlend" line of its Part A printout: the tokens with the largest
+  layer-0 hidden-state drift are the ones recomputed.
 
 Where the pages leave a step open, the plainest reading is taken; each such
 reading is marked "Reading:" below.
@@ -523,3 +526,57 @@ def kv_bytes(layers, kv_heads, head_dim, tokens, bytes_per_elem):
     """KV bytes = 2 * layers * kv_heads * head_dim * tokens * bytes_per_element
     (KV-handoff module, section 1)."""
     return 2 * layers * kv_heads * head_dim * tokens * bytes_per_elem
+
+
+# ---------------------------------------------------------------------------
+# Recompute selection after a chunk reorder (the CacheBlend step)
+# ---------------------------------------------------------------------------
+# The HyperCache post, Core Design, recompute paragraph: layer 0's KV is exact
+# after the rotation, and the tokens whose layer-0 hidden state drifts the
+# most, about 15% of them, are recomputed through the deeper layers.  Part A
+# of its printout reports the "15% CacheBlend" configuration.
+# Reading: the drift of token t is the Euclidean norm of the difference of
+# its two layer-0 hidden states (fresh context minus cached context); the
+# selection is the k largest drifts, ties going to the lower token index and
+# NaN ranking above every number; +0 and -0 are equal.  The list is returned
+# in increasing token order (the order a recompute pass gathers them in).
+
+def token_drift(h_cached, h_fresh):
+    """Per-token drift ||h_fresh[t] - h_cached[t]||_2 over the last axis, in
+    float64 (inputs of any binary format convert exactly).
+
+    Pinned by: Pythagorean rows with integer norms, math.hypot row by row on
+    random data, symmetry, zero for equal rows, exact scaling by powers of
+    two, and the triangle inequality."""
+    a = np.asarray(h_cached, dtype=np.float64)
+    b = np.asarray(h_fresh, dtype=np.float64)
+    d = b - a
+    return np.sqrt(np.sum(d * d, axis=-1))
+
+
+def recompute_count(n_tokens, percent=15):
+    """Reading: k = floor(percent * n / 100) tokens are recomputed (the post
+    says "about 15%").
+
+    Pinned by: small cases written out, and k / n within 1 / n of 15%."""
+    return (int(n_tokens) * int(percent)) // 100
+
+
+def select_top_tokens(drift, k):
+    """Indices (int32, increasing) of the k tokens with the largest drift.
+
+    Order: larger value first; NaN above everything; equal values (+0 and
+    -0 included) by lower index.  k must lie in [0, n].
+
+    Pinned by: a brute-force search over all k-subsets of tiny inputs for
+    the set that outranks its complement, and worked cases (all equal,
+    k = 0, k = n, NaN, signed zeros, negative values)."""
+    v = np.asarray(drift, dtype=np.float64).reshape(-1)
+    n = v.size
+    if not 0 <= k <= n:
+        raise ValueError(f"k={k} outside [0, {n}]")
+    nan = np.isnan(v)
+    value = np.where(nan, 0.0, v)
+    # np.lexsort: the last key is the primary one, each ascending
+    ranked = np.lexsort((np.arange(n), -value, ~nan))
+    return np.sort(ranked[:k]).astype(np.int32)

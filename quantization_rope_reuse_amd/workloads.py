@@ -231,3 +231,97 @@ def pages_from_tokens(x: np.ndarray, w: KVWorkload, table: np.ndarray) -> np.nda
     pages = np.zeros((int(table.max()) + 1 if table.size else 0,) + blocks.shape[1:], x.dtype)
     pages[table] = blocks
     return pages
+
+
+# ---------------------------------------------------------------------------
+# Layer-0 hidden states for the recompute selection
+# ---------------------------------------------------------------------------
+# A reused prefix is a list of chunks; the reorder moves every chunk after
+# the leading system chunk.  The cached hidden states are N(0, 1).  The fresh
+# ones equal them exactly on the leading chunk (same tokens at the same
+# positions after the same predecessors) and elsewhere add N(0, sigma_t^2)
+# noise, sigma_t = 0.05 * (1 + 4 exp(-j / 64)) * exp(0.5 z_t), j the token's
+# offset in its chunk and z_t ~ N(0, 1): drift is largest right after a chunk
+# boundary and log-normally spread, with a block of exact zeros (ties).
+
+@dataclasses.dataclass(frozen=True)
+class DriftWorkload:
+    name: str
+    lead_tokens: int            # the unmoved leading chunk
+    chunk_tokens: int           # every later chunk
+    n_chunks: int               # later chunks
+    d_model: int
+    dtype: str                  # "f32" | "f16" | "bf16"
+    percent: int = 15
+    seed: int = 0
+
+    @property
+    def n_tokens(self) -> int:
+        return self.lead_tokens + self.n_chunks * self.chunk_tokens
+
+
+# The GQA reorder's reused prefix [Sys 256, DocB 512, DocA 512] with a
+# 32-query-head x 128 model width; Qwen3-8B (4096 wide, fp16) and
+# Llama-3-70B (8192 wide, bf16) prefixes of 32k and 64k tokens.
+DRIFT_GQA = DriftWorkload(name="drift_gqa_1280tok_4096_fp32", lead_tokens=256,
+                          chunk_tokens=512, n_chunks=2, d_model=4096, dtype="f32")
+DRIFT_QWEN3_8B = DriftWorkload(name="drift_qwen3_8b_32768tok_4096_fp16", lead_tokens=1024,
+                               chunk_tokens=1024, n_chunks=31, d_model=4096, dtype="f16")
+DRIFT_LLAMA3_70B = DriftWorkload(name="drift_llama3_70b_65536tok_8192_bf16", lead_tokens=2048,
+                                 chunk_tokens=2048, n_chunks=31, d_model=8192, dtype="bf16")
+DRIFT_ALL = (DRIFT_GQA, DRIFT_QWEN3_8B, DRIFT_LLAMA3_70B)
+
+
+def drift_sigma(w: DriftWorkload) -> np.ndarray:
+    """Per-token noise scale sigma_t (float32 [n_tokens]); 0 on the lead chunk."""
+    z = np.random.default_rng(_seed_words(w.seed, 401, w.n_tokens)).standard_normal(
+        w.n_tokens)
+    j = (np.arange(w.n_tokens) - w.lead_tokens) % w.chunk_tokens
+    s = 0.05 * (1.0 + 4.0 * np.exp(-j / 64.0)) * np.exp(0.5 * z)
+    s[:w.lead_tokens] = 0.0
+    return s.astype(np.float32)
+
+
+def _round_dtype(x: np.ndarray, dtype: str) -> np.ndarray:
+    """float32 -> the workload dtype, as float32 values (bf16 by RNE on the
+    bit pattern)."""
+    if dtype == "f32":
+        return x.astype(np.float32)
+    if dtype == "f16":
+        return x.astype(np.float16).astype(np.float32)
+    u = x.astype(np.float32).view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16 << 16
+    return u.astype(np.uint32).view(np.float32)
+
+
+def host_hidden_states(w: DriftWorkload):
+    """(cached, fresh) float32 [n_tokens, d_model] holding values of the
+    workload dtype, on the host."""
+    g = np.random.default_rng(_seed_words(w.seed, 402, w.n_tokens))
+    cached = _round_dtype(g.standard_normal((w.n_tokens, w.d_model), dtype=np.float32), w.dtype)
+    noise = g.standard_normal((w.n_tokens, w.d_model), dtype=np.float32)
+    fresh = _round_dtype(cached + drift_sigma(w)[:, None] * noise, w.dtype)
+    return cached, fresh
+
+
+def device_hidden_states(w: DriftWorkload, device, rows_per_step: int = 4096):
+    """(cached, fresh) torch tensors [n_tokens, d_model] of the workload dtype
+    drawn on `device`, row slab by row slab."""
+    import torch
+    dt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[w.dtype]
+    cached = torch.empty((w.n_tokens, w.d_model), dtype=dt, device=device)
+    fresh = torch.empty_like(cached)
+    sigma = torch.from_numpy(drift_sigma(w)).to(device)
+    g = torch.Generator(device=device)
+    h = hashlib.sha256(f"{w.name}:{w.seed}:hidden".encode()).digest()
+    g.manual_seed(int.from_bytes(h[:8], "little") & ((1 << 63) - 1))
+    tmp = torch.empty((rows_per_step, w.d_model), dtype=torch.float32, device=device)
+    for r0 in range(0, w.n_tokens, rows_per_step):
+        r1 = min(w.n_tokens, r0 + rows_per_step)
+        t = tmp[:r1 - r0]
+        t.normal_(0.0, 1.0, generator=g)
+        c = t.to(dt)
+        cached[r0:r1] = c
+        t.normal_(0.0, 1.0, generator=g)
+        fresh[r0:r1] = (c.float() + sigma[r0:r1, None] * t).to(dt)
+    return cached, fresh

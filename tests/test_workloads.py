@@ -63,3 +63,29 @@ def test_pages_from_tokens():
     t = np.array([2, 0, 3, 1])
     p = W.pages_from_tokens(x, w, t)
     assert np.array_equal(p[2], x[0:16]) and np.array_equal(p[1], x[48:64])
+
+
+def test_drift_workloads():
+    assert [w.n_tokens for w in W.DRIFT_ALL] == [1280, 32768, 65536]
+    w = W.DRIFT_GQA
+    s = W.drift_sigma(w)
+    assert not s[:w.lead_tokens].any() and (s[w.lead_tokens:] > 0).all()
+    # largest right after a chunk boundary, on average
+    j = (np.arange(w.n_tokens) - w.lead_tokens) % w.chunk_tokens
+    body = s[w.lead_tokens:]
+    jj = j[w.lead_tokens:]
+    assert body[jj < 16].mean() > 3 * body[jj > 256].mean()
+    c, f = W.host_hidden_states(w)
+    c2, f2 = W.host_hidden_states(w)
+    assert np.array_equal(c, c2) and np.array_equal(f, f2)
+    assert c.shape == (1280, 4096) and c.dtype == np.float32
+    assert np.array_equal(c[:w.lead_tokens], f[:w.lead_tokens])
+    assert (np.abs(f - c)[w.lead_tokens:].max(axis=1) > 0).all()
+
+
+def test_drift_bf16_rounding_is_rne():
+    x = np.array([1.0, 1.0 + 2.0**-8, 1.0 + 3 * 2.0**-8, 1.0 + 2.0**-9, -2.5e-3], np.float32)
+    got = W._round_dtype(x, "bf16")
+    assert got.tolist()[:4] == [1.0, 1.0, 1.0 + 2.0**-6, 1.0]
+    assert (got.view(np.uint32) & 0xFFFF == 0).all()
+    assert abs(got[4] - x[4]) <= 2.0**-9 * abs(x[4])

@@ -247,6 +247,8 @@ def main():
         torch.cuda.synchronize()
         del x, y
 
+    select = recompute_select(dev, hkv, W)
+
     cpu = None
     if not a.no_cpu_baseline:
         cpu = cpu_baseline(w, records_bytes=rb, budget_s=a.cpu_seconds)
@@ -300,9 +302,52 @@ def main():
                 "gbps": round(put_bytes / (float(np.mean(put_ms)) * 1e-3) / 1e9, 1)},
         "crc32": {"mean_ms_incl_stream_handoff": round(float(np.mean(crc_ms)), 4),
                   "gbps": round(crc_bytes / (float(np.mean(crc_ms)) * 1e-3) / 1e9, 1)},
+        "recompute_select": select,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
+
+
+def recompute_select(dev, hkv, W, reps=10):
+    """The recompute selection on a Llama-3-70B-width prefix (65,536 tokens x
+    8,192 bf16): per-token layer-0 drift, then the top 15%.  Outside the
+    step; timed with HIP events on the current stream.  Algorithmic bytes of
+    the drift: both rows read (2 * 8192 * 2 per token) plus the fp32 drift."""
+    import numpy as np
+    import torch
+    w = W.DRIFT_LLAMA3_70B
+    cached, fresh = W.device_hidden_states(w, dev)
+    drift = torch.empty(w.n_tokens, dtype=torch.float32, device=dev)
+    k = (w.n_tokens * w.percent) // 100
+    sel = torch.empty(k, dtype=torch.int32, device=dev)
+    s = torch.cuda.current_stream(dev)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    drift_ms, sel_ms = [], []
+    for rep in range(reps + 2):
+        ev[0].record(s)
+        hkv.token_drift(cached, fresh, out=drift, stream=s)
+        ev[1].record(s)
+        hkv.select_top_tokens(drift, k, out=sel, stream=s)
+        ev[2].record(s)
+        s.synchronize()
+        if rep >= 2:
+            drift_ms.append(ev[0].elapsed_time(ev[1]))
+            sel_ms.append(ev[1].elapsed_time(ev[2]))
+    es = cached.element_size()
+    drift_bytes = w.n_tokens * (2 * w.d_model * es + 4)
+    dms = float(np.mean(drift_ms))
+    gbps = drift_bytes / (dms * 1e-3) / 1e9
+    del cached, fresh
+    torch.cuda.empty_cache()
+    return {
+        "workload": f"{w.n_tokens} tokens x {w.d_model} {w.dtype} layer-0 hidden states, "
+                    f"top {w.percent}% (k={k})",
+        "drift_ms": round(dms, 4),
+        "drift_gbps": round(gbps, 1),
+        "drift_frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4),
+        "drift_alg_bytes": drift_bytes,
+        "select_ms": round(float(np.mean(sel_ms)), 4),
+    }
 
 
 def overlap(a, w, L, hkv, rec_l, ok_l, ov_l, ftab, dm, order, side):

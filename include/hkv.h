@@ -200,6 +200,37 @@ int hkv_stream_pair_create(int32_t fetch_cus, hipStream_t* fetch_stream,
                            hipStream_t* compute_stream);
 int hkv_stream_destroy(hipStream_t stream);
 
+/* Recompute selection after a chunk reorder (HyperCache post, Core Design,
+ * recompute paragraph; Part A, the "15% CacheBlend" line): the layer-0 KV
+ * is exact after the rotation, and the tokens whose layer-0 hidden state
+ * moved the most between the cached and the fresh context are the ones
+ * recomputed through the deeper layers.
+ *
+ * Step 1, drift.  For t < n_tokens:
+ *   drift_out[t] = sqrt( sum_j (h_fresh[t][j] - h_cached[t][j])^2 ),
+ * j < d_model, element (t, j) at h + t*row_stride + j (row_stride in
+ * ELEMENTS, shared by both arrays; dtype HKV_F32/F16/BF16).  Differences,
+ * squares and the sum are fp32 (one accumulator per lane over
+ * d_model/64 elements, then a 64-way tree), so the relative error is at most
+ * about (d_model/64 + 10) * 2^-24.  h_cached, h_fresh: device, 16-byte
+ * aligned, row_stride * element size a multiple of 16 and >= d_model when
+ * n_tokens > 1.  drift_out: float [n_tokens], device.  n_tokens = 0 is an
+ * empty call; d_model = 0 gives zeros (the row pointers may then be NULL). */
+int hkv_token_drift(const void* h_cached, const void* h_fresh, int32_t n_tokens,
+                    int32_t d_model, int64_t row_stride, int32_t dtype, float* drift_out,
+                    hipStream_t stream);
+
+/* Step 2, selection.  Writes to selected_out (int32 [k], device) the indices
+ * of the k largest values of drift (float [n_tokens], device) in increasing
+ * index order.  Order: a larger value first; NaN above every number; equal
+ * values (+0 and -0 are equal) by lower index, so the result is unique.
+ * 0 <= k <= n_tokens (k = 0 writes nothing).  The caller picks k; the post
+ * recomputes about 15% of the tokens.  One workgroup does the whole
+ * selection in five passes over drift: meant for up to a few hundred
+ * thousand tokens. */
+int hkv_select_top_tokens(const float* drift, int32_t n_tokens, int32_t k,
+                          int32_t* selected_out, hipStream_t stream);
+
 /* Host-only helpers. */
 
 /* Bytes of one record: 2*N*C + 4*N (see hkv_records); -1 on bad arguments. */

@@ -22,7 +22,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libhkv.so")
-SOURCES = ("api.hip", "quant.hip", "fetch.hip", "crc.hip", "order.hip", "streams.hip")
+SOURCES = ("api.hip", "quant.hip", "fetch.hip", "crc.hip", "order.hip", "streams.hip",
+           "select.hip")
 ARCH = "gfx950"
 
 

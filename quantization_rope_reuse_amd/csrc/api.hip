@@ -200,4 +200,30 @@ int hkv_crc32_blocks(const hkv_shape* shape, int32_t fmt, const hkv_records* src
   return to_status(hkv::launch_crc32(g, rb, rv, crc_out, stream));
 }
 
+int hkv_token_drift(const void* h_cached, const void* h_fresh, int32_t n_tokens,
+                    int32_t d_model, int64_t row_stride, int32_t dtype, float* drift_out,
+                    hipStream_t stream) {
+  const int es = elem_size(dtype);
+  if (es == 0 || n_tokens < 0 || d_model < 0 || row_stride < 0) return HKV_ERR_INVALID_ARG;
+  if (n_tokens == 0) return HKV_OK;
+  if (!drift_out || ((!h_cached || !h_fresh) && d_model > 0)) return HKV_ERR_INVALID_ARG;
+  if (!aligned16(h_cached) || !aligned16(h_fresh)) return HKV_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(drift_out) & 3u) != 0) return HKV_ERR_INVALID_ARG;
+  if (row_stride > INT64_MAX / 8 || (row_stride * es) % 16 != 0) return HKV_ERR_INVALID_ARG;
+  if (n_tokens > 1 && row_stride < d_model) return HKV_ERR_INVALID_ARG;
+  return to_status(hkv::launch_drift(dtype, h_cached, h_fresh, n_tokens, d_model,
+                                     row_stride * es, drift_out, stream));
+}
+
+int hkv_select_top_tokens(const float* drift, int32_t n_tokens, int32_t k,
+                          int32_t* selected_out, hipStream_t stream) {
+  if (n_tokens < 0 || k < 0 || k > n_tokens) return HKV_ERR_INVALID_ARG;
+  if (k == 0) return HKV_OK;
+  if (!drift || !selected_out) return HKV_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(drift) & 3u) != 0 ||
+      (reinterpret_cast<uintptr_t>(selected_out) & 3u) != 0)
+    return HKV_ERR_INVALID_ARG;
+  return to_status(hkv::launch_topk(drift, n_tokens, k, selected_out, stream));
+}
+
 }  // extern "C"

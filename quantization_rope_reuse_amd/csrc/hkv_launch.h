@@ -43,4 +43,10 @@ hipError_t launch_page_order(const int32_t* table, int32_t n_blocks, int32_t num
 hipError_t launch_crc32(const Geometry& g, int64_t record_bytes, const RecordView& src,
                         uint32_t* out, hipStream_t stream);
 
+hipError_t launch_drift(int dtype, const void* cached, const void* fresh, int32_t n_tokens,
+                        int32_t d_model, int64_t row_bytes, float* drift, hipStream_t stream);
+
+hipError_t launch_topk(const float* drift, int32_t n, int32_t k, int32_t* selected,
+                       hipStream_t stream);
+
 }  // namespace hkv

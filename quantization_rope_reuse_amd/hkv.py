@@ -87,13 +87,16 @@ def lib():
             P(Pages), ctypes.c_int32, vp]
         l.hkv_page_visit_order.argtypes = [vp, ctypes.c_int32, ctypes.c_int32, vp, vp]
         l.hkv_crc32_blocks.argtypes = [P(Shape), ctypes.c_int32, P(Records), vp, vp]
+        l.hkv_token_drift.argtypes = [vp, vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
+                                      ctypes.c_int32, vp, vp]
+        l.hkv_select_top_tokens.argtypes = [vp, ctypes.c_int32, ctypes.c_int32, vp, vp]
         l.hkv_stream_pair_create.argtypes = [ctypes.c_int32, P(vp), P(vp)]
         l.hkv_stream_pair_create.restype = ctypes.c_int
         l.hkv_stream_destroy.argtypes = [vp]
         l.hkv_stream_destroy.restype = ctypes.c_int
         for name in ("hkv_quant_fp8", "hkv_quant_int4", "hkv_fetch_dequant_rope_shift",
                      "hkv_fetch_dequant_rope_shift_tokens", "hkv_crc32_blocks",
-                     "hkv_page_visit_order"):
+                     "hkv_page_visit_order", "hkv_token_drift", "hkv_select_top_tokens"):
             getattr(l, name).restype = ctypes.c_int
         l.hkv_record_bytes.argtypes = [ctypes.c_int32] * 4
         l.hkv_record_bytes.restype = ctypes.c_int64
@@ -285,4 +288,42 @@ def crc32_blocks(records, fmt, block_tokens: int, n_kv_heads: int, out=None, str
     st = lib().hkv_crc32_blocks(ctypes.byref(shape), FORMATS[fmt], ctypes.byref(rec),
                                 ctypes.c_void_p(out.data_ptr()), _stream(stream, records.device))
     _check("hkv_crc32_blocks", st)
+    return out
+
+
+def token_drift(h_cached, h_fresh, out=None, stream=None):
+    """Per-token drift ||h_fresh[t] - h_cached[t]||_2 of two [n_tokens, d_model]
+    tensors (same dtype, same row stride, last axis contiguous); returns a
+    float32 tensor [n_tokens]."""
+    if h_cached.shape != h_fresh.shape or h_cached.dim() != 2:
+        raise ValueError("hidden states must be two [n_tokens, d_model] tensors of one shape")
+    if h_cached.dtype != h_fresh.dtype or h_cached.dtype not in TORCH_DTYPES:
+        raise ValueError("hidden states must share an f32/f16/bf16 dtype")
+    if h_cached.stride() != h_fresh.stride() or (h_cached.shape[1] > 1 and h_cached.stride(1) != 1):
+        raise ValueError("hidden states must share row strides, last axis contiguous")
+    n, d = h_cached.shape
+    if out is None:
+        out = torch.empty(n, dtype=torch.float32, device=h_cached.device)
+    if out.dtype != torch.float32 or not out.is_contiguous() or out.numel() != n:
+        raise ValueError("out must be a contiguous float32 tensor of n_tokens elements")
+    st = lib().hkv_token_drift(ctypes.c_void_p(h_cached.data_ptr()),
+                               ctypes.c_void_p(h_fresh.data_ptr()), n, d,
+                               h_cached.stride(0), TORCH_DTYPES[h_cached.dtype],
+                               ctypes.c_void_p(out.data_ptr()), _stream(stream, h_cached.device))
+    _check("hkv_token_drift", st)
+    return out
+
+
+def select_top_tokens(drift, k: int, out=None, stream=None):
+    """Indices of the k largest drift values, increasing; int32 tensor [k]."""
+    if drift.dtype != torch.float32 or not drift.is_contiguous():
+        raise ValueError("drift must be a contiguous float32 tensor")
+    n = drift.numel()
+    if out is None:
+        out = torch.empty(max(int(k), 0), dtype=torch.int32, device=drift.device)
+    if out.numel() < k:
+        raise ValueError("out must hold k entries")
+    st = lib().hkv_select_top_tokens(ctypes.c_void_p(drift.data_ptr()), n, int(k),
+                                     _i32(out, "out"), _stream(stream, drift.device))
+    _check("hkv_select_top_tokens", st)
     return out

@@ -15,7 +15,8 @@ def test_exports_every_declared_symbol():
     assert set(names) == {"hkv_quant_fp8", "hkv_quant_int4", "hkv_fetch_dequant_rope_shift",
                           "hkv_crc32_blocks", "hkv_record_bytes", "hkv_status_string",
                           "hkv_page_visit_order", "hkv_fetch_dequant_rope_shift_tokens",
-                          "hkv_stream_pair_create", "hkv_stream_destroy"}
+                          "hkv_stream_pair_create", "hkv_stream_destroy", "hkv_token_drift",
+                          "hkv_select_top_tokens"}
     lib = H.lib()
     for n in names:
         assert getattr(lib, n) is not None
@@ -186,3 +187,55 @@ def test_binding_validates_tensors_before_calling():
     with pytest.raises(ValueError):
         H.quant_fp8(k, k, torch.zeros(4, dtype=torch.int64),
                     torch.zeros((1, 4, 33280), dtype=torch.uint8))
+
+
+def _drift(a=FAKE, b=FAKE + 4096, n=4, d=4096, stride=4096, dt=2, out=FAKE + 8192):
+    return H.lib().hkv_token_drift(ctypes.c_void_p(a), ctypes.c_void_p(b), n, d, stride, dt,
+                                   ctypes.c_void_p(out), None)
+
+
+BAD_DRIFT = [
+    ("bad dtype", dict(dt=3)),
+    ("negative tokens", dict(n=-1)),
+    ("negative width", dict(d=-8)),
+    ("null cached", dict(a=0)),
+    ("null fresh", dict(b=0)),
+    ("null out", dict(out=0)),
+    ("misaligned cached", dict(a=FAKE + 8)),
+    ("misaligned out", dict(out=FAKE + 2)),
+    ("row stride not 16 bytes", dict(stride=4100)),
+    ("row stride below width", dict(stride=2048)),
+    ("negative stride", dict(stride=-4096)),
+]
+
+
+@pytest.mark.parametrize("name,kw", BAD_DRIFT, ids=[b[0] for b in BAD_DRIFT])
+def test_drift_rejects_bad_arguments(name, kw):
+    assert _drift(**kw) == H.ERR_INVALID_ARG
+
+
+def test_select_rejects_bad_arguments():
+    lib = H.lib()
+    call = lambda d=FAKE, n=100, k=15, o=FAKE + 4096: lib.hkv_select_top_tokens(
+        ctypes.c_void_p(d), n, k, ctypes.c_void_p(o), None)
+    assert call(k=101) == H.ERR_INVALID_ARG
+    assert call(k=-1) == H.ERR_INVALID_ARG
+    assert call(n=-1, k=0) == H.ERR_INVALID_ARG
+    assert call(d=0) == H.ERR_INVALID_ARG
+    assert call(o=0) == H.ERR_INVALID_ARG
+    assert call(d=FAKE + 2) == H.ERR_INVALID_ARG
+    assert call(k=0, d=0, o=0) == H.OK               # empty: nothing launched
+    assert _drift(n=0, a=0, b=0, out=0) == H.OK
+    # one row: the stride is not used; zero width: the rows are not read
+    assert _drift(n=1, stride=0, a=0) == H.ERR_INVALID_ARG
+    assert _drift(n=3, d=0, stride=0, a=0, b=0, out=0) == H.ERR_INVALID_ARG
+
+
+def test_selection_binding_validates_tensors():
+    import torch
+    with pytest.raises(ValueError):
+        H.select_top_tokens(torch.zeros(8, dtype=torch.float64), 2)
+    with pytest.raises(ValueError):
+        H.token_drift(torch.zeros((4, 8)), torch.zeros((4, 8), dtype=torch.float16))
+    with pytest.raises(ValueError):
+        H.token_drift(torch.zeros((4, 8)), torch.zeros((4, 9)))

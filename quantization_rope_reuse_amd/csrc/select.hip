@@ -15,13 +15,15 @@
 // topk_kernel: one workgroup of 1024 threads.  Each value is mapped to a
 // 32-bit key whose unsigned order is the selection order (NaN highest, -0 as
 // +0).  The key of the k-th largest value is found by a most-significant-
-// digit-first radix select: four passes of 8 bits, each building a 256-bin
-// LDS histogram of the keys that still match the digits chosen so far, after
-// which one wave finds the bin holding the k-th key with a suffix scan.
-// A last pass over tiles of 1024 tokens writes every token whose key is above
-// that threshold, and the lowest-indexed tokens equal to it, at the position
-// given by the count of selected tokens before it (wave ballots plus a
-// 16-entry LDS scan per tile), so the output is in increasing token order.
+// digit-first radix select: three passes over the keys with digits of 11, 11
+// and 10 bits, each building a 2048-bin LDS histogram of the keys that still
+// match the digits chosen so far, after which one wave finds the bin holding
+// the k-th key with a suffix scan.  A last pass writes every token whose key
+// is above that threshold, and the lowest-indexed tokens equal to it, at the
+// position given by the number of selected tokens before it (wave ballots
+// plus a block scan per batch of 16 keys per thread), so the output is in
+// increasing token order.  Keys are read in batches of 16 independent loads
+// per thread, so each pass waits for memory once per batch.
 #include "hkv_device.h"
 #include "hkv_launch.h"
 
@@ -110,54 +112,96 @@ __device__ __forceinline__ uint32_t order_key(float x) {
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
+// Adds one to hist[d] for every lane with `live` set.  Keys of nearby values
+// share a digit, so the wave's two most common digits among the first lanes
+// are added with one atomic each and only the remaining lanes one by one.
+__device__ __forceinline__ void wave_histogram_add(int* hist, bool live, uint32_t d, int lane) {
+  uint64_t todo = __ballot(live);
+#pragma unroll
+  for (int it = 0; it < 2; ++it) {
+    if (todo == 0) return;
+    const int leader = __builtin_ctzll(todo);
+    const uint32_t dl = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(d), leader));
+    const uint64_t same = __ballot(live && d == dl);   // a subset of todo
+    if (lane == leader) atomicAdd(&hist[dl], __popcll(same));
+    todo &= ~same;
+  }
+  if ((todo >> lane) & 1u) atomicAdd(&hist[d], 1);
+}
+
 __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* drift, int32_t n,
                                                              int32_t k, int32_t* selected) {
-  __shared__ int hist[256];
-  __shared__ int wave_count[2][2][kTopkWaves];      // [tile parity][above, equal][wave]
+  constexpr int kSlots = 16;                         // keys per thread per batch
+  constexpr int kBatch = kSlots * kTopkThreads;      // token b0 + r * 1024 + tid in slot r
+  constexpr int kEntries = kSlots * kTopkWaves;      // (slot, wave) counts per batch, in token order
+  constexpr int kBins = 2048;
+  __shared__ __align__(16) int hist[kBins];
+  __shared__ int count_a[kEntries];
+  __shared__ int count_e[kEntries];
+  __shared__ int wave_sum[2][kTopkWaves];
   __shared__ uint32_t s_prefix;
   __shared__ int s_remaining;
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
 
-  // Radix select.  Invariant: 1 <= remaining <= number of keys matching
-  // `prefix` under `mask`; remaining counts how many of them are still to be
-  // taken, the keys above them all being taken already.
+  // Radix select, digits of 11, 11 and 10 bits.  Invariant: 1 <= remaining
+  // <= number of keys matching `prefix` under `mask`; the keys above those
+  // are all taken, and `remaining` more are to be taken among them.
   uint32_t prefix = 0, mask = 0;
   int remaining = k;
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    if (tid < 256) hist[tid] = 0;
+#pragma unroll 1
+  for (int pass = 0; pass < 3; ++pass) {
+    const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
+    const uint32_t dmask = pass == 2 ? 0x3FFu : 0x7FFu;
+    hist[tid] = 0;
+    hist[tid + kTopkThreads] = 0;
     __syncthreads();
-    for (int i = tid; i < n; i += kTopkThreads) {
-      const uint32_t key = order_key(drift[i]);
-      if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 0xFFu], 1);
+    for (int b0 = 0; b0 < n; b0 += kBatch) {
+      uint32_t key[kSlots];
+#pragma unroll
+      for (int r = 0; r < kSlots; ++r) {
+        const int i = b0 + r * kTopkThreads + tid;
+        key[r] = i < n ? order_key(drift[i]) : 0u;
+      }
+#pragma unroll
+      for (int r = 0; r < kSlots; ++r) {
+        const bool live = b0 + r * kTopkThreads + tid < n && (key[r] & mask) == prefix;
+        wave_histogram_add(hist, live, (key[r] >> shift) & dmask, lane);
+      }
     }
     __syncthreads();
     if (wave == 0) {
-      // lane l holds bins 4l..4l+3; suffix sums run from the top bin down
-      const int c0 = hist[4 * lane], c1 = hist[4 * lane + 1];
-      const int c2 = hist[4 * lane + 2], c3 = hist[4 * lane + 3];
-      const int s = c0 + c1 + c2 + c3;
-      int suf = s;
+      // lane l holds bins 32l .. 32l+31, read as eight 4-bin groups; suffix
+      // sums run from the top bin down
+      const int4* h4 = reinterpret_cast<const int4*>(hist) + 8 * lane;
+      int sum = 0;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int4 v = h4[q];
+        sum += v.x + v.y + v.z + v.w;
+      }
+      int suf = sum;
 #pragma unroll
       for (int off = 1; off < kWave; off <<= 1) {
         const int up = __shfl_down(suf, off);
         if (lane + off < kWave) suf += up;
       }
-      int above = suf - s;                          // keys in the bins of higher lanes
-      if (above < remaining && remaining <= suf) {  // exactly one lane
-        int d;
-        if (above + c3 >= remaining) {
-          d = 4 * lane + 3;
-        } else if (above + c3 + c2 >= remaining) {
-          above += c3;
-          d = 4 * lane + 2;
-        } else if (above + c3 + c2 + c1 >= remaining) {
-          above += c3 + c2;
-          d = 4 * lane + 1;
-        } else {
-          above += c3 + c2 + c1;
-          d = 4 * lane;
+      int above = suf - sum;                          // keys in the bins of higher lanes
+      if (above < remaining && remaining <= suf) {    // exactly one lane
+        int d = 32 * lane;
+        for (int q = 7; q >= 0; --q) {
+          const int4 v = h4[q];
+          const int c[4] = {v.x, v.y, v.z, v.w};
+          int j = 3;
+          for (; j >= 0; --j) {
+            if (above + c[j] >= remaining) break;
+            above += c[j];
+          }
+          if (j >= 0) {
+            d = 32 * lane + 4 * q + j;
+            break;
+          }
         }
         s_prefix = prefix | (static_cast<uint32_t>(d) << shift);
         s_remaining = remaining - above;
@@ -166,40 +210,82 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* drift, 
     __syncthreads();
     prefix = s_prefix;
     remaining = s_remaining;
-    mask |= 0xFFu << shift;
+    mask |= dmask << shift;
   }
   const uint32_t thr = prefix;          // key of the k-th largest value
   // remaining = how many keys equal to thr are taken: the lowest-indexed ones
 
+  // Output, batch by batch: the selected tokens before token i are the keys
+  // above thr before it plus min(keys equal to thr before it, remaining).
   const uint64_t below = lane == 0 ? 0ull : (~0ull >> (kWave - lane));
-  int above_done = 0, equal_done = 0;   // counts over earlier tiles
-  for (int t0 = 0, par = 0; t0 < n; t0 += kTopkThreads, par ^= 1) {
-    const int i = t0 + tid;
-    const uint32_t key = i < n ? order_key(drift[i]) : 0u;
-    const bool is_above = i < n && key > thr;
-    const bool is_equal = i < n && key == thr;
-    const uint64_t m_above = __ballot(is_above);
-    const uint64_t m_equal = __ballot(is_equal);
-    if (lane == 0) {
-      wave_count[par][0][wave] = __popcll(m_above);
-      wave_count[par][1][wave] = __popcll(m_equal);
+  int done_a = 0, done_e = 0;           // counts over earlier batches
+  for (int b0 = 0; b0 < n; b0 += kBatch) {
+    uint32_t key[kSlots];
+#pragma unroll
+    for (int r = 0; r < kSlots; ++r) {
+      const int i = b0 + r * kTopkThreads + tid;
+      key[r] = i < n ? order_key(drift[i]) : 0u;
+    }
+#pragma unroll
+    for (int r = 0; r < kSlots; ++r) {
+      const bool valid = b0 + r * kTopkThreads + tid < n;
+      const uint64_t ma = __ballot(valid && key[r] > thr);
+      const uint64_t me = __ballot(valid && key[r] == thr);
+      if (lane == 0) {
+        count_a[r * kTopkWaves + wave] = __popcll(ma);
+        count_e[r * kTopkWaves + wave] = __popcll(me);
+      }
     }
     __syncthreads();
-    int above_before = above_done + __popcll(m_above & below);
-    int equal_before = equal_done + __popcll(m_equal & below);
+    // exclusive scan over the kEntries entries, entry e held by thread e
+    const int va = tid < kEntries ? count_a[tid] : 0;
+    const int ve = tid < kEntries ? count_e[tid] : 0;
+    int ia = va, ie = ve;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+      const int ua = __shfl_up(ia, off);
+      const int ue = __shfl_up(ie, off);
+      if (lane >= off) {
+        ia += ua;
+        ie += ue;
+      }
+    }
+    if (lane == kWave - 1) {
+      wave_sum[0][wave] = ia;
+      wave_sum[1][wave] = ie;
+    }
+    __syncthreads();
+    int base_a = 0, base_e = 0, total_a = 0, total_e = 0;
 #pragma unroll
     for (int w = 0; w < kTopkWaves; ++w) {
-      const int ca = wave_count[par][0][w];
-      const int ce = wave_count[par][1][w];
-      above_before += w < wave ? ca : 0;
-      equal_before += w < wave ? ce : 0;
-      above_done += ca;
-      equal_done += ce;
+      const int sa = wave_sum[0][w];
+      const int se = wave_sum[1][w];
+      base_a += w < wave ? sa : 0;
+      base_e += w < wave ? se : 0;
+      total_a += sa;
+      total_e += se;
     }
-    const int pos = above_before + min(equal_before, remaining);
-    if ((is_above || (is_equal && equal_before < remaining)) && pos < k) selected[pos] = i;
-    // the other buffer is written next; this one again only after the next
-    // tile's barrier, which every thread reaches after its reads here
+    if (tid < kEntries) {
+      count_a[tid] = done_a + base_a + ia - va;
+      count_e[tid] = done_e + base_e + ie - ve;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < kSlots; ++r) {
+      const int i = b0 + r * kTopkThreads + tid;
+      const bool valid = i < n;
+      const bool is_above = valid && key[r] > thr;
+      const bool is_equal = valid && key[r] == thr;
+      const uint64_t ma = __ballot(is_above);
+      const uint64_t me = __ballot(is_equal);
+      const int above_before = count_a[r * kTopkWaves + wave] + __popcll(ma & below);
+      const int equal_before = count_e[r * kTopkWaves + wave] + __popcll(me & below);
+      const int pos = above_before + min(equal_before, remaining);
+      if ((is_above || (is_equal && equal_before < remaining)) && pos < k) selected[pos] = i;
+    }
+    done_a += total_a;
+    done_e += total_e;
+    __syncthreads();                    // count_* and wave_sum are rewritten next batch
   }
 }
 

@@ -580,3 +580,139 @@ def select_top_tokens(drift, k):
     # np.lexsort: the last key is the primary one, each ascending
     ranked = np.lexsort((np.arange(n), -value, ~nan))
     return np.sort(ranked[:k]).astype(np.int32)
+
+
+# ---------------------------------------------------------------------------
+# Self-describing frames (record container)
+# ---------------------------------------------------------------------------
+# The HyperCache post's FP8 wire frame and INT4 disk file carry headers of 68
+# and 69 bytes around the payload (Part B byte counts) whose layout it does not
+# give.  Reading: a 64-byte little-endian header of our own precedes each
+# record, so a frame names its shape, its place in the cache and the cached
+# position of its first token (what a reader needs for the relative shift
+# dm = m_new - m_old), and carries the record's CRC-32 and a CRC-32 of the
+# header itself:
+#    0 u32 magic 0x46564B48 ("HKVF")   4 u16 version 1   6 u16 header bytes 64
+#    8 u8 format (0 FP8, 1 INT4)       9 u8 zero         10 u16 head_dim
+#   12 u16 block_tokens               14 u16 n_kv_heads
+#   16 u32 layer   20 u32 block   24 i32 m_old   28 u32 payload bytes
+#   32 u32 payload CRC-32   36..59 zero   60 u32 CRC-32 of bytes 0..59
+
+FRAME_HEADER_BYTES = 64
+FRAME_MAGIC = 0x46564B48
+FRAME_VERSION = 1
+# verification flags
+FRAME_BAD_MAGIC = 1
+FRAME_BAD_HEADER_CRC = 2
+FRAME_BAD_GEOMETRY = 4
+FRAME_BAD_INDEX = 8
+FRAME_BAD_PAYLOAD_CRC = 16
+
+
+def _u32(b, off):
+    return int(b[off]) | int(b[off + 1]) << 8 | int(b[off + 2]) << 16 | int(b[off + 3]) << 24
+
+
+def _put_u(b, off, value, n):
+    for j in range(n):
+        b[off + j] = (int(value) >> (8 * j)) & 0xFF
+
+
+def frame_header(fmt, block_tokens, n_kv_heads, layer, block, m_old, payload_bytes,
+                 payload_crc, head_dim=HEAD_DIM):
+    """The 64 header bytes of one frame (uint8 [64]).
+
+    Pinned by: a header spelled out byte by byte from the layout above, the
+    header CRC against zlib, and parse_frame_header round trips."""
+    b = np.zeros(FRAME_HEADER_BYTES, dtype=np.uint8)
+    _put_u(b, 0, FRAME_MAGIC, 4)
+    _put_u(b, 4, FRAME_VERSION, 2)
+    _put_u(b, 6, FRAME_HEADER_BYTES, 2)
+    b[8] = 0 if fmt == FMT_FP8 else 1
+    _put_u(b, 10, head_dim, 2)
+    _put_u(b, 12, block_tokens, 2)
+    _put_u(b, 14, n_kv_heads, 2)
+    _put_u(b, 16, layer, 4)
+    _put_u(b, 20, block, 4)
+    _put_u(b, 24, int(m_old) & 0xFFFFFFFF, 4)
+    _put_u(b, 28, payload_bytes, 4)
+    _put_u(b, 32, payload_crc, 4)
+    _put_u(b, 60, int(crc32_records(b[None, :60])[0]), 4)
+    return b
+
+
+def parse_frame_header(b):
+    """Field dictionary of a 64-byte header (no checks)."""
+    b = np.asarray(b, dtype=np.uint8)
+    m_old = _u32(b, 24)
+    return {
+        "magic": _u32(b, 0), "version": int(b[4]) | int(b[5]) << 8,
+        "header_bytes": int(b[6]) | int(b[7]) << 8, "format": int(b[8]),
+        "head_dim": int(b[10]) | int(b[11]) << 8,
+        "block_tokens": int(b[12]) | int(b[13]) << 8,
+        "n_kv_heads": int(b[14]) | int(b[15]) << 8,
+        "layer": _u32(b, 16), "block": _u32(b, 20),
+        "m_old": m_old - (1 << 32) if m_old >= 1 << 31 else m_old,
+        "payload_bytes": _u32(b, 28), "payload_crc": _u32(b, 32),
+        "header_crc": _u32(b, 60),
+    }
+
+
+def make_frames(records, fmt, block_tokens, n_kv_heads, m_old, layer_base=0):
+    """Frames [L, n_blocks, 64 + record bytes] for records [L, n_blocks, bytes]
+    and the cached positions m_old [n_blocks] (shared by the layers)."""
+    rec = np.asarray(records, dtype=np.uint8)
+    L, nb, rb = rec.shape
+    crc = crc32_records(rec)
+    out = np.zeros((L, nb, FRAME_HEADER_BYTES + rb), dtype=np.uint8)
+    for l in range(L):
+        for b in range(nb):
+            out[l, b, :FRAME_HEADER_BYTES] = frame_header(
+                fmt, block_tokens, n_kv_heads, layer_base + l, b, int(m_old[b]), rb,
+                int(crc[l, b]))
+    out[:, :, FRAME_HEADER_BYTES:] = rec
+    return out
+
+
+def verify_frames(frames, fmt, block_tokens, n_kv_heads, layer_base=0):
+    """Flags per frame (uint32 [L, n_blocks]); 0 means the frame is intact and
+    belongs at (layer_base + l, b) of a cache of this shape and format.
+
+    Pinned by: intact frames give 0; each kind of damage (magic, a header
+    field, the header CRC word, a payload byte, a frame moved to another
+    slot) raises its own flag."""
+    fr = np.asarray(frames, dtype=np.uint8)
+    L, nb, _ = fr.shape
+    rb = record_bytes(fmt, block_tokens, n_kv_heads)
+    payload_crc = crc32_records(fr[:, :, FRAME_HEADER_BYTES:FRAME_HEADER_BYTES + rb])
+    head_crc = crc32_records(fr[:, :, :60])
+    out = np.zeros((L, nb), dtype=np.uint32)
+    for l in range(L):
+        for b in range(nb):
+            h = parse_frame_header(fr[l, b, :FRAME_HEADER_BYTES])
+            f = 0
+            if (h["magic"], h["version"], h["header_bytes"]) != \
+                    (FRAME_MAGIC, FRAME_VERSION, FRAME_HEADER_BYTES):
+                f |= FRAME_BAD_MAGIC
+            if h["header_crc"] != int(head_crc[l, b]):
+                f |= FRAME_BAD_HEADER_CRC
+            if (h["format"], h["head_dim"], h["block_tokens"], h["n_kv_heads"],
+                    h["payload_bytes"]) != (0 if fmt == FMT_FP8 else 1, HEAD_DIM, block_tokens,
+                                            n_kv_heads, rb):
+                f |= FRAME_BAD_GEOMETRY
+            if (h["layer"], h["block"]) != (layer_base + l, b):
+                f |= FRAME_BAD_INDEX
+            if h["payload_crc"] != int(payload_crc[l, b]):
+                f |= FRAME_BAD_PAYLOAD_CRC
+            out[l, b] = f
+    return out
+
+
+def frame_delta_m(frames, m_new):
+    """dm[b] = m_new[b] - m_old of the first layer's frame b (the relative
+    shift of the HyperCache post's relative-RoPE paragraph), clamped to int32."""
+    fr = np.asarray(frames, dtype=np.uint8)
+    m_old = np.array([parse_frame_header(fr[0, b, :FRAME_HEADER_BYTES])["m_old"]
+                      for b in range(fr.shape[1])], dtype=np.int64)
+    d = np.asarray(m_new, dtype=np.int64) - m_old
+    return np.clip(d, -(1 << 31), (1 << 31) - 1).astype(np.int32)

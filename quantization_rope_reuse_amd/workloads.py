@@ -184,6 +184,21 @@ def delta_m(w: KVWorkload) -> np.ndarray:
     raise ValueError(w.delta_kind)
 
 
+def block_positions(w: KVWorkload):
+    """(m_old, m_new) int32 [n_blocks]: the cached and the reused position of
+    each logical block's first token, with m_new - m_old = delta_m(w).  Cached
+    positions are the blocks' own token offsets (the reorder workload: their
+    offsets in the cached order), raised by a common base so that no reused
+    position is negative."""
+    dm = delta_m(w).astype(np.int64)
+    if w.delta_kind == "reorder":
+        m_old = reorder_plan(w)[0].astype(np.int64) * w.block_tokens
+    else:
+        m_old = np.arange(w.n_blocks, dtype=np.int64) * w.block_tokens
+    m_old += max(0, int(-(m_old + dm).min()))
+    return m_old.astype(np.int32), (m_old + dm).astype(np.int32)
+
+
 def reorder_plan(w: KVWorkload):
     """GQA reorder: for each block of the reused order, the block index it had
     in the cached order and its delta.  Returns (old_block[n_blocks],

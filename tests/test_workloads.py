@@ -89,3 +89,15 @@ def test_drift_bf16_rounding_is_rne():
     assert got.tolist()[:4] == [1.0, 1.0, 1.0 + 2.0**-6, 1.0]
     assert (got.view(np.uint32) & 0xFFFF == 0).all()
     assert abs(got[4] - x[4]) <= 2.0**-9 * abs(x[4])
+
+
+def test_block_positions():
+    for w in W.ALL:
+        m_old, m_new = W.block_positions(w)
+        assert np.array_equal(m_new.astype(np.int64) - m_old, W.delta_m(w))
+        assert m_new.min() >= 0 and m_old.min() >= 0
+    m_old, m_new = W.block_positions(W.GQA_REORDER)
+    # DocB's first block sat after Sys + DocA in the cached order and moves to 256
+    assert m_old[16] == 768 and m_new[16] == 256
+    m_old, _ = W.block_positions(W.LLAMA3_70B)
+    assert m_old[1] - m_old[0] == 64

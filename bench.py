@@ -247,6 +247,7 @@ def main():
         torch.cuda.synchronize()
         del x, y
 
+    frames = frames_leg(dev, hkv, W, w, L, src_k, src_v, put_tab)
     select = recompute_select(dev, hkv, W)
 
     cpu = None
@@ -302,10 +303,56 @@ def main():
                 "gbps": round(put_bytes / (float(np.mean(put_ms)) * 1e-3) / 1e9, 1)},
         "crc32": {"mean_ms_incl_stream_handoff": round(float(np.mean(crc_ms)), 4),
                   "gbps": round(crc_bytes / (float(np.mean(crc_ms)) * 1e-3) / 1e9, 1)},
+        "frames": frames,
         "recompute_select": select,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
+
+
+def frames_leg(dev, hkv, W, w, L, src_k, src_v, put_tab, reps=3):
+    """The same cache as self-describing frames (64-byte header + record):
+    put into the frames' records, CRC, header writing, and a full
+    verification (CRC of every record again plus the header checks).
+    Outside the step; HIP events on the current stream."""
+    import numpy as np
+    import torch
+    nb, tb, H = w.n_blocks, w.block_tokens, w.n_kv_heads
+    frames = hkv.alloc_frames(L, nb, "fp8", tb, H, device=dev)
+    rec = hkv.frame_records(frames)
+    crc = torch.empty((L, nb), dtype=torch.int32, device=dev)
+    flags = torch.empty((L, nb), dtype=torch.int32, device=dev)
+    m_old = torch.from_numpy(W.block_positions(w)[0]).to(dev)
+    s = torch.cuda.current_stream(dev)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    hdr_ms, ver_ms = [], []
+    for rep in range(reps + 1):
+        ev[0].record(s)
+        hkv.quant_fp8(src_k, src_v, put_tab, rec, stream=s)
+        hkv.crc32_blocks(rec, "fp8", tb, H, out=crc, stream=s)
+        ev[1].record(s)
+        hkv.frame_headers(frames, "fp8", tb, H, crc, m_old, stream=s)
+        ev[2].record(s)
+        hkv.frame_verify(frames, "fp8", tb, H, out=flags, stream=s)
+        ev[3].record(s)
+        s.synchronize()
+        if rep:
+            hdr_ms.append(ev[1].elapsed_time(ev[2]))
+            ver_ms.append(ev[2].elapsed_time(ev[3]))
+    if bool(flags.any()):
+        raise RuntimeError("frame verification flagged intact frames")
+    rb = hkv.record_bytes("fp8", tb, H)
+    verify_bytes = L * nb * (rb + 64 + 4)
+    vms = float(np.mean(ver_ms))
+    del frames, rec
+    torch.cuda.empty_cache()
+    return {
+        "frames": L * nb,
+        "frame_bytes": 64 + rb,
+        "headers_ms": round(float(np.mean(hdr_ms)), 4),
+        "verify_ms": round(vms, 4),
+        "verify_gbps": round(verify_bytes / (vms * 1e-3) / 1e9, 1),
+    }
 
 
 def recompute_select(dev, hkv, W, reps=10):

@@ -200,6 +200,57 @@ int hkv_stream_pair_create(int32_t fetch_cus, hipStream_t* fetch_stream,
                            hipStream_t* compute_stream);
 int hkv_stream_destroy(hipStream_t stream);
 
+/* Self-describing frames (HyperCache post: Part B, the FP8 wire frame and
+ * the INT4 disk file, both a header around the payload; the post prints
+ * their sizes but not their layout, so the header is this library's own).
+ * A frame is a 64-byte header followed by the record of one (layer, block);
+ * `frames` describes the frames as hkv_records does records (the record of
+ * frame (l, b) starts HKV_FRAME_HEADER_BYTES after it, so the same buffer
+ * serves put, CRC and fetch through a records view at base + 64).  Each
+ * frame must hold header + record: block and layer strides >= 64 +
+ * hkv_record_bytes() (when there is more than one), multiples of 16.
+ * block_tokens and n_kv_heads must fit 16 bits (else HKV_ERR_UNSUPPORTED).
+ * Header, little endian:
+ *    0 u32 magic 0x46564B48 ("HKVF")  4 u16 version 1  6 u16 header bytes 64
+ *    8 u8 format (0 FP8, 1 INT4)  9 u8 0  10 u16 head_dim
+ *   12 u16 block_tokens  14 u16 n_kv_heads  16 u32 layer  20 u32 block
+ *   24 i32 m_old (cached position of the block's first token)
+ *   28 u32 record bytes  32 u32 record CRC-32  36..59 zero
+ *   60 u32 CRC-32 of bytes 0..59 (zlib variant, as hkv_crc32_blocks) */
+#define HKV_FRAME_HEADER_BYTES 64
+
+/* Flags written by hkv_frame_verify (0 = intact and in its place). */
+#define HKV_FRAME_BAD_MAGIC 1u        /* magic, version or header size     */
+#define HKV_FRAME_BAD_HEADER_CRC 2u   /* header bytes 0..59 vs their CRC   */
+#define HKV_FRAME_BAD_GEOMETRY 4u     /* format, head_dim, block_tokens,
+                                         n_kv_heads or record bytes differ
+                                         from the call's                   */
+#define HKV_FRAME_BAD_INDEX 8u        /* layer or block field is not the
+                                         frame's slot                      */
+#define HKV_FRAME_BAD_PAYLOAD_CRC 16u /* record bytes vs the stored CRC    */
+
+/* Writes the header of every frame (l, b): layer = layer_base + l, block =
+ * b, m_old[b] (int32 [n_blocks], device, shared by the layers), the record's
+ * CRC crc[l * n_blocks + b] (uint32, device, as hkv_crc32_blocks writes it
+ * for the records view).  Record bytes are not touched. */
+int hkv_frame_headers(const hkv_shape* shape, int32_t fmt, const hkv_records* frames,
+                      const uint32_t* crc, const int32_t* m_old, int32_t layer_base,
+                      hipStream_t stream);
+
+/* Checks every frame against the call's shape and format and its slot
+ * (layer_base + l, b): recomputes the record's CRC-32 and the header's, and
+ * writes the HKV_FRAME_BAD_* flags to status_out (uint32 [n_layers *
+ * n_blocks], device, layer-major). */
+int hkv_frame_verify(const hkv_shape* shape, int32_t fmt, const hkv_records* frames,
+                     int32_t layer_base, uint32_t* status_out, hipStream_t stream);
+
+/* delta_out[b] = m_new[b] - m_old of frame (0, b), clamped to the int32
+ * range: the per-block delta for hkv_fetch_dequant_rope_shift (HyperCache
+ * post, relative-RoPE paragraph: dm = m_new - m_old).  m_new, delta_out:
+ * int32 [n_blocks], device.  Reads only the first layer's headers. */
+int hkv_frame_delta_m(const hkv_shape* shape, int32_t fmt, const hkv_records* frames,
+                      const int32_t* m_new, int32_t* delta_out, hipStream_t stream);
+
 /* Recompute selection after a chunk reorder (HyperCache post, Core Design,
  * recompute paragraph; Part A, the "15% CacheBlend" line): the layer-0 KV
  * is exact after the rotation, and the tokens whose layer-0 hidden state

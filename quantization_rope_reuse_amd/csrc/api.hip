@@ -90,6 +90,29 @@ int check_records(const hkv_records* r, int32_t fmt, const hkv_shape* s, RecordV
 
 int to_status(hipError_t e) { return e == hipSuccess ? HKV_OK : HKV_ERR_HIP; }
 
+// Frames: the records view describes the frames; each frame must hold the
+// header and the record.  Fills the launch geometry and the frame view.
+int check_frames(const hkv_shape* shape, int32_t fmt, const hkv_records* frames, Geometry* g,
+                 RecordView* v, int64_t* rb) {
+  int st;
+  if (!valid_format(fmt)) return HKV_ERR_INVALID_ARG;
+  if ((st = check_shape(shape, g)) != HKV_OK) return st;
+  if (shape->block_tokens > 65535 || shape->n_kv_heads > 65535) return HKV_ERR_UNSUPPORTED;
+  if (!frames || !frames->base || !aligned16(frames->base)) return HKV_ERR_INVALID_ARG;
+  if (frames->layer_stride_bytes < 0 || frames->block_stride_bytes < 0 ||
+      frames->layer_stride_bytes % 16 != 0 || frames->block_stride_bytes % 16 != 0)
+    return HKV_ERR_INVALID_ARG;
+  *rb = hkv_record_bytes(fmt, shape->block_tokens, shape->n_kv_heads, shape->head_dim);
+  const int64_t fb = *rb + hkv::kFrameHeaderBytes;
+  if (shape->n_blocks > 1 && frames->block_stride_bytes < fb) return HKV_ERR_INVALID_ARG;
+  if (shape->n_layers > 1 && frames->layer_stride_bytes < fb) return HKV_ERR_INVALID_ARG;
+  if (*rb > (int64_t{1} << 30)) return HKV_ERR_UNSUPPORTED;
+  v->base = static_cast<uint8_t*>(frames->base);
+  v->layer = frames->layer_stride_bytes;
+  v->block = frames->block_stride_bytes;
+  return HKV_OK;
+}
+
 int quant_common(int32_t fmt, const hkv_shape* shape, const hkv_pages* src, int32_t src_dtype,
                  const int32_t* block_table, const hkv_records* dst, hipStream_t stream) {
   Geometry g;
@@ -198,6 +221,45 @@ int hkv_crc32_blocks(const hkv_shape* shape, int32_t fmt, const hkv_records* src
                                       shape->head_dim);
   if (rb > (int64_t{1} << 30)) return HKV_ERR_UNSUPPORTED;
   return to_status(hkv::launch_crc32(g, rb, rv, crc_out, stream));
+}
+
+int hkv_frame_headers(const hkv_shape* shape, int32_t fmt, const hkv_records* frames,
+                      const uint32_t* crc, const int32_t* m_old, int32_t layer_base,
+                      hipStream_t stream) {
+  Geometry g;
+  RecordView v;
+  int64_t rb;
+  int st;
+  if ((st = check_frames(shape, fmt, frames, &g, &v, &rb)) != HKV_OK) return st;
+  if (layer_base < 0) return HKV_ERR_INVALID_ARG;
+  if (g.n_layers == 0 || g.n_blocks == 0) return HKV_OK;
+  if (!crc || !m_old) return HKV_ERR_INVALID_ARG;
+  return to_status(hkv::launch_frame_headers(fmt, g, v, rb, layer_base, crc, m_old, stream));
+}
+
+int hkv_frame_verify(const hkv_shape* shape, int32_t fmt, const hkv_records* frames,
+                     int32_t layer_base, uint32_t* status_out, hipStream_t stream) {
+  Geometry g;
+  RecordView v;
+  int64_t rb;
+  int st;
+  if ((st = check_frames(shape, fmt, frames, &g, &v, &rb)) != HKV_OK) return st;
+  if (layer_base < 0) return HKV_ERR_INVALID_ARG;
+  if (g.n_layers == 0 || g.n_blocks == 0) return HKV_OK;
+  if (!status_out) return HKV_ERR_INVALID_ARG;
+  return to_status(hkv::launch_frame_verify(fmt, g, v, rb, layer_base, status_out, stream));
+}
+
+int hkv_frame_delta_m(const hkv_shape* shape, int32_t fmt, const hkv_records* frames,
+                      const int32_t* m_new, int32_t* delta_out, hipStream_t stream) {
+  Geometry g;
+  RecordView v;
+  int64_t rb;
+  int st;
+  if ((st = check_frames(shape, fmt, frames, &g, &v, &rb)) != HKV_OK) return st;
+  if (g.n_layers == 0 || g.n_blocks == 0) return HKV_OK;
+  if (!m_new || !delta_out) return HKV_ERR_INVALID_ARG;
+  return to_status(hkv::launch_frame_delta(g, v, m_new, delta_out, stream));
 }
 
 int hkv_token_drift(const void* h_cached, const void* h_fresh, int32_t n_tokens,

@@ -43,6 +43,20 @@ hipError_t launch_page_order(const int32_t* table, int32_t n_blocks, int32_t num
 hipError_t launch_crc32(const Geometry& g, int64_t record_bytes, const RecordView& src,
                         uint32_t* out, hipStream_t stream);
 
+// Frames: a kFrameHeaderBytes header, then the record.
+constexpr int64_t kFrameHeaderBytes = 64;
+
+hipError_t launch_frame_headers(int fmt, const Geometry& g, const RecordView& frames,
+                                int64_t record_bytes, int32_t layer_base, const uint32_t* crc,
+                                const int32_t* m_old, hipStream_t stream);
+
+hipError_t launch_frame_verify(int fmt, const Geometry& g, const RecordView& frames,
+                               int64_t record_bytes, int32_t layer_base, uint32_t* status,
+                               hipStream_t stream);
+
+hipError_t launch_frame_delta(const Geometry& g, const RecordView& frames, const int32_t* m_new,
+                              int32_t* delta, hipStream_t stream);
+
 hipError_t launch_drift(int dtype, const void* cached, const void* fresh, int32_t n_tokens,
                         int32_t d_model, int64_t row_bytes, float* drift, hipStream_t stream);
 

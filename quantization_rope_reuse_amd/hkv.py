@@ -90,13 +90,19 @@ def lib():
         l.hkv_token_drift.argtypes = [vp, vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
                                       ctypes.c_int32, vp, vp]
         l.hkv_select_top_tokens.argtypes = [vp, ctypes.c_int32, ctypes.c_int32, vp, vp]
+        l.hkv_frame_headers.argtypes = [P(Shape), ctypes.c_int32, P(Records), vp, vp,
+                                        ctypes.c_int32, vp]
+        l.hkv_frame_verify.argtypes = [P(Shape), ctypes.c_int32, P(Records), ctypes.c_int32,
+                                       vp, vp]
+        l.hkv_frame_delta_m.argtypes = [P(Shape), ctypes.c_int32, P(Records), vp, vp, vp]
         l.hkv_stream_pair_create.argtypes = [ctypes.c_int32, P(vp), P(vp)]
         l.hkv_stream_pair_create.restype = ctypes.c_int
         l.hkv_stream_destroy.argtypes = [vp]
         l.hkv_stream_destroy.restype = ctypes.c_int
         for name in ("hkv_quant_fp8", "hkv_quant_int4", "hkv_fetch_dequant_rope_shift",
                      "hkv_fetch_dequant_rope_shift_tokens", "hkv_crc32_blocks",
-                     "hkv_page_visit_order", "hkv_token_drift", "hkv_select_top_tokens"):
+                     "hkv_page_visit_order", "hkv_token_drift", "hkv_select_top_tokens",
+                     "hkv_frame_headers", "hkv_frame_verify", "hkv_frame_delta_m"):
             getattr(l, name).restype = ctypes.c_int
         l.hkv_record_bytes.argtypes = [ctypes.c_int32] * 4
         l.hkv_record_bytes.restype = ctypes.c_int64
@@ -326,4 +332,76 @@ def select_top_tokens(drift, k: int, out=None, stream=None):
     st = lib().hkv_select_top_tokens(ctypes.c_void_p(drift.data_ptr()), n, int(k),
                                      _i32(out, "out"), _stream(stream, drift.device))
     _check("hkv_select_top_tokens", st)
+    return out
+
+
+FRAME_HEADER_BYTES = 64
+FRAME_BAD_MAGIC, FRAME_BAD_HEADER_CRC, FRAME_BAD_GEOMETRY = 1, 2, 4
+FRAME_BAD_INDEX, FRAME_BAD_PAYLOAD_CRC = 8, 16
+
+
+def alloc_frames(n_layers: int, n_blocks: int, fmt, block_tokens: int, n_kv_heads: int,
+                 device="cuda"):
+    """A uint8 [L, n_blocks, 64 + record_bytes] tensor of frames (frame stride
+    rounded up to 16 bytes)."""
+    fb = FRAME_HEADER_BYTES + record_bytes(fmt, block_tokens, n_kv_heads)
+    stride = (fb + 15) // 16 * 16
+    buf = torch.empty((n_layers, n_blocks, stride), dtype=torch.uint8, device=device)
+    return buf[:, :, :fb]
+
+
+def frame_records(frames):
+    """The records inside frames: a view for the put, CRC and fetch calls."""
+    return frames[:, :, FRAME_HEADER_BYTES:]
+
+
+def _frame_args(frames, fmt, block_tokens, n_kv_heads):
+    if frames.dim() != 3:
+        raise ValueError("frames must be a uint8 [L, n_blocks, bytes] tensor")
+    shape = Shape(frames.shape[0], frames.shape[1], block_tokens, n_kv_heads, HEAD_DIM)
+    return shape, _records(frames)
+
+
+def frame_headers(frames, fmt, block_tokens: int, n_kv_heads: int, crc, m_old,
+                  layer_base: int = 0, stream=None):
+    """Write the header of every frame (records and their CRCs already there)."""
+    shape, fr = _frame_args(frames, fmt, block_tokens, n_kv_heads)
+    if crc.numel() != frames.shape[0] * frames.shape[1] or m_old.numel() != frames.shape[1]:
+        raise ValueError("crc must hold L * n_blocks entries and m_old n_blocks")
+    st = lib().hkv_frame_headers(ctypes.byref(shape), FORMATS[fmt], ctypes.byref(fr),
+                                 _i32(crc, "crc"), _i32(m_old, "m_old"), int(layer_base),
+                                 _stream(stream, frames.device))
+    _check("hkv_frame_headers", st)
+    return frames
+
+
+def frame_verify(frames, fmt, block_tokens: int, n_kv_heads: int, layer_base: int = 0,
+                 out=None, stream=None):
+    """Verification flags per frame: an int32 tensor [L, n_blocks] (0 = intact)."""
+    shape, fr = _frame_args(frames, fmt, block_tokens, n_kv_heads)
+    L, nb = frames.shape[0], frames.shape[1]
+    if out is None:
+        out = torch.empty((L, nb), dtype=torch.int32, device=frames.device)
+    if out.numel() != L * nb:
+        raise ValueError("out must hold L * n_blocks entries")
+    st = lib().hkv_frame_verify(ctypes.byref(shape), FORMATS[fmt], ctypes.byref(fr),
+                                int(layer_base), _i32(out, "out"),
+                                _stream(stream, frames.device))
+    _check("hkv_frame_verify", st)
+    return out
+
+
+def frame_delta_m(frames, fmt, block_tokens: int, n_kv_heads: int, m_new, out=None,
+                  stream=None):
+    """Per-block delta m_new - m_old from the first layer's frame headers."""
+    shape, fr = _frame_args(frames, fmt, block_tokens, n_kv_heads)
+    nb = frames.shape[1]
+    if out is None:
+        out = torch.empty(nb, dtype=torch.int32, device=frames.device)
+    if out.numel() != nb or m_new.numel() != nb:
+        raise ValueError("m_new and out must hold n_blocks entries")
+    st = lib().hkv_frame_delta_m(ctypes.byref(shape), FORMATS[fmt], ctypes.byref(fr),
+                                 _i32(m_new, "m_new"), _i32(out, "out"),
+                                 _stream(stream, frames.device))
+    _check("hkv_frame_delta_m", st)
     return out

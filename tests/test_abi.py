@@ -16,7 +16,8 @@ def test_exports_every_declared_symbol():
                           "hkv_crc32_blocks", "hkv_record_bytes", "hkv_status_string",
                           "hkv_page_visit_order", "hkv_fetch_dequant_rope_shift_tokens",
                           "hkv_stream_pair_create", "hkv_stream_destroy", "hkv_token_drift",
-                          "hkv_select_top_tokens"}
+                          "hkv_select_top_tokens", "hkv_frame_headers", "hkv_frame_verify",
+                          "hkv_frame_delta_m"}
     lib = H.lib()
     for n in names:
         assert getattr(lib, n) is not None
@@ -239,3 +240,51 @@ def test_selection_binding_validates_tensors():
         H.token_drift(torch.zeros((4, 8)), torch.zeros((4, 8), dtype=torch.float16))
     with pytest.raises(ValueError):
         H.token_drift(torch.zeros((4, 8)), torch.zeros((4, 9)))
+
+
+def _frames_view(**kw):
+    d = dict(base=FAKE, layer_stride_bytes=4 * 33344, block_stride_bytes=33344)
+    d.update(kw)
+    return H.Records(**d)
+
+
+def test_frame_calls_reject_bad_arguments():
+    lib = H.lib()
+    s = _shape()                                       # 16 tokens x 8 heads: 33,280 B records
+    hdr = lambda fr, crc=FAKE, m=FAKE, lb=0, fmt=0, sh=s: lib.hkv_frame_headers(
+        ctypes.byref(sh), fmt, ctypes.byref(fr), ctypes.c_void_p(crc), ctypes.c_void_p(m), lb,
+        None)
+    # a frame stride that cannot hold header + record
+    assert hdr(_frames_view(block_stride_bytes=33280)) == H.ERR_INVALID_ARG
+    assert hdr(_frames_view(layer_stride_bytes=33280, block_stride_bytes=33344)) == \
+        H.ERR_INVALID_ARG
+    assert hdr(_frames_view(base=FAKE + 8)) == H.ERR_INVALID_ARG
+    assert hdr(_frames_view(block_stride_bytes=33352)) == H.ERR_INVALID_ARG   # not 16-B
+    assert hdr(_frames_view(), crc=0) == H.ERR_INVALID_ARG
+    assert hdr(_frames_view(), m=0) == H.ERR_INVALID_ARG
+    assert hdr(_frames_view(), lb=-1) == H.ERR_INVALID_ARG
+    assert hdr(_frames_view(), fmt=5) == H.ERR_INVALID_ARG
+    assert hdr(_frames_view(), sh=_shape(block_tokens=70000, n_kv_heads=1)) == \
+        H.ERR_UNSUPPORTED
+    assert hdr(_frames_view(), sh=_shape(n_blocks=0), crc=0, m=0) == H.OK
+    ver = lambda fr, out=FAKE, lb=0: lib.hkv_frame_verify(
+        ctypes.byref(s), 0, ctypes.byref(fr), lb, ctypes.c_void_p(out), None)
+    assert ver(_frames_view(), out=0) == H.ERR_INVALID_ARG
+    assert ver(_frames_view(), lb=-3) == H.ERR_INVALID_ARG
+    assert ver(_frames_view(block_stride_bytes=16)) == H.ERR_INVALID_ARG
+    dl = lambda fr, m=FAKE, out=FAKE: lib.hkv_frame_delta_m(
+        ctypes.byref(s), 0, ctypes.byref(fr), ctypes.c_void_p(m), ctypes.c_void_p(out), None)
+    assert dl(_frames_view(), m=0) == H.ERR_INVALID_ARG
+    assert dl(_frames_view(), out=0) == H.ERR_INVALID_ARG
+    assert dl(_frames_view(base=0)) == H.ERR_INVALID_ARG
+
+
+def test_frame_allocation_shapes():
+    import torch
+    fr = H.alloc_frames(2, 3, "fp8", 16, 8, device="cpu")
+    assert fr.shape == (2, 3, 64 + 33280) and fr.stride(1) == 33344
+    rec = H.frame_records(fr)
+    assert rec.shape == (2, 3, 33280) and rec.data_ptr() == fr.data_ptr() + 64
+    fr4 = H.alloc_frames(1, 2, "int4", 1, 1, device="cpu")
+    assert fr4.shape[2] == 64 + 132 and fr4.stride(1) == 208
+    assert fr.dtype == torch.uint8

@@ -237,6 +237,9 @@ def main():
               flush=True)
         return
 
+    frames = frames_leg(dev, hkv, W, w, L, src_k, src_v, put_tab)
+    select = recompute_select(dev, hkv, W)
+
     if a.calibrate_copy:
         # torch.neg over 2**28 fp32 values: reads exactly 1 GiB, writes 1 GiB
         del src_k, src_v, out_k, out_v, records
@@ -246,9 +249,6 @@ def main():
             torch.neg(x, out=y)
         torch.cuda.synchronize()
         del x, y
-
-    frames = frames_leg(dev, hkv, W, w, L, src_k, src_v, put_tab)
-    select = recompute_select(dev, hkv, W)
 
     cpu = None
     if not a.no_cpu_baseline:

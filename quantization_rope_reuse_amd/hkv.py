@@ -342,12 +342,15 @@ FRAME_BAD_INDEX, FRAME_BAD_PAYLOAD_CRC = 8, 16
 
 def alloc_frames(n_layers: int, n_blocks: int, fmt, block_tokens: int, n_kv_heads: int,
                  device="cuda"):
-    """A uint8 [L, n_blocks, 64 + record_bytes] tensor of frames (frame stride
-    rounded up to 16 bytes)."""
+    """A uint8 [L, n_blocks, 64 + record_bytes] tensor of frames.  The frame
+    stride is a multiple of 128 bytes and the frames start 64 bytes into a
+    128-byte aligned allocation, so every record starts on a 128-byte line."""
     fb = FRAME_HEADER_BYTES + record_bytes(fmt, block_tokens, n_kv_heads)
-    stride = (fb + 15) // 16 * 16
-    buf = torch.empty((n_layers, n_blocks, stride), dtype=torch.uint8, device=device)
-    return buf[:, :, :fb]
+    stride = (fb + 127) // 128 * 128
+    n = n_layers * n_blocks * stride
+    buf = torch.empty(n + 128, dtype=torch.uint8, device=device)
+    skip = (64 - buf.data_ptr()) % 128
+    return buf[skip:skip + n].view(n_layers, n_blocks, stride)[:, :, :fb]
 
 
 def frame_records(frames):

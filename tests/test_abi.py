@@ -282,9 +282,10 @@ def test_frame_calls_reject_bad_arguments():
 def test_frame_allocation_shapes():
     import torch
     fr = H.alloc_frames(2, 3, "fp8", 16, 8, device="cpu")
-    assert fr.shape == (2, 3, 64 + 33280) and fr.stride(1) == 33344
+    assert fr.shape == (2, 3, 64 + 33280) and fr.stride(1) == 33408 and fr.stride(0) == 3 * 33408
     rec = H.frame_records(fr)
     assert rec.shape == (2, 3, 33280) and rec.data_ptr() == fr.data_ptr() + 64
+    assert rec.data_ptr() % 128 == 0 and fr.data_ptr() % 128 == 64
     fr4 = H.alloc_frames(1, 2, "int4", 1, 1, device="cpu")
-    assert fr4.shape[2] == 64 + 132 and fr4.stride(1) == 208
+    assert fr4.shape[2] == 64 + 132 and fr4.stride(1) == 256
     assert fr.dtype == torch.uint8

@@ -275,12 +275,23 @@ int hkv_token_drift(const void* h_cached, const void* h_fresh, int32_t n_tokens,
  * of the k largest values of drift (float [n_tokens], device) in increasing
  * index order.  Order: a larger value first; NaN above every number; equal
  * values (+0 and -0 are equal) by lower index, so the result is unique.
- * 0 <= k <= n_tokens (k = 0 writes nothing).  The caller picks k; the post
- * recomputes about 15% of the tokens.  One workgroup does the whole
- * selection in five passes over drift: meant for up to a few hundred
- * thousand tokens. */
+ * 0 <= k <= n_tokens <= 2^30 (k = 0 writes nothing; more tokens:
+ * HKV_ERR_UNSUPPORTED).  The caller picks k; the post recomputes about 15%
+ * of the tokens.
+ * workspace: NULL, or 16-byte aligned device memory of at least
+ * hkv_select_workspace_bytes(n_tokens) bytes (workspace_bytes says how many).
+ * Without it one workgroup makes four passes over drift (fine for a few
+ * thousand tokens, ~2 ns per token beyond); with it the passes are spread
+ * over up to 64 workgroups in five launches.  The workspace holds no state
+ * between calls; calls that share one must not overlap. */
 int hkv_select_top_tokens(const float* drift, int32_t n_tokens, int32_t k,
-                          int32_t* selected_out, hipStream_t stream);
+                          int32_t* selected_out, void* workspace, int64_t workspace_bytes,
+                          hipStream_t stream);
+
+/* Workspace bytes for hkv_select_top_tokens over n_tokens values (about
+ * 24 KiB per 4,096 tokens up to 64k tokens, at most 1.6 MB); -1 if n_tokens
+ * is negative or above 2^30. */
+int64_t hkv_select_workspace_bytes(int32_t n_tokens);
 
 /* Host-only helpers. */
 

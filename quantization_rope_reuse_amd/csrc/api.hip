@@ -90,6 +90,8 @@ int check_records(const hkv_records* r, int32_t fmt, const hkv_shape* s, RecordV
 
 int to_status(hipError_t e) { return e == hipSuccess ? HKV_OK : HKV_ERR_HIP; }
 
+constexpr int32_t kMaxSelectTokens = 1 << 30;
+
 // Frames: the records view describes the frames; each frame must hold the
 // header and the record.  Fills the launch geometry and the frame view.
 int check_frames(const hkv_shape* shape, int32_t fmt, const hkv_records* frames, Geometry* g,
@@ -277,15 +279,25 @@ int hkv_token_drift(const void* h_cached, const void* h_fresh, int32_t n_tokens,
                                      row_stride * es, drift_out, stream));
 }
 
+int64_t hkv_select_workspace_bytes(int32_t n_tokens) {
+  if (n_tokens < 0 || n_tokens > kMaxSelectTokens) return -1;
+  return hkv::select_workspace_bytes(n_tokens);
+}
+
 int hkv_select_top_tokens(const float* drift, int32_t n_tokens, int32_t k,
-                          int32_t* selected_out, hipStream_t stream) {
+                          int32_t* selected_out, void* workspace, int64_t workspace_bytes,
+                          hipStream_t stream) {
   if (n_tokens < 0 || k < 0 || k > n_tokens) return HKV_ERR_INVALID_ARG;
+  if (n_tokens > kMaxSelectTokens) return HKV_ERR_UNSUPPORTED;
+  if (workspace && (!aligned16(workspace) ||
+                    workspace_bytes < hkv::select_workspace_bytes(n_tokens)))
+    return HKV_ERR_INVALID_ARG;
   if (k == 0) return HKV_OK;
   if (!drift || !selected_out) return HKV_ERR_INVALID_ARG;
   if ((reinterpret_cast<uintptr_t>(drift) & 3u) != 0 ||
       (reinterpret_cast<uintptr_t>(selected_out) & 3u) != 0)
     return HKV_ERR_INVALID_ARG;
-  return to_status(hkv::launch_topk(drift, n_tokens, k, selected_out, stream));
+  return to_status(hkv::launch_topk(drift, n_tokens, k, selected_out, workspace, stream));
 }
 
 }  // extern "C"

@@ -60,7 +60,11 @@ hipError_t launch_frame_delta(const Geometry& g, const RecordView& frames, const
 hipError_t launch_drift(int dtype, const void* cached, const void* fresh, int32_t n_tokens,
                         int32_t d_model, int64_t row_bytes, float* drift, hipStream_t stream);
 
+// Workspace of the many-workgroup selection for n values.
+int64_t select_workspace_bytes(int32_t n);
+
+// workspace: NULL (one workgroup) or select_workspace_bytes(n) bytes.
 hipError_t launch_topk(const float* drift, int32_t n, int32_t k, int32_t* selected,
-                       hipStream_t stream);
+                       void* workspace, hipStream_t stream);
 
 }  // namespace hkv

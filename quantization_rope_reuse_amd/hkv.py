@@ -89,7 +89,10 @@ def lib():
         l.hkv_crc32_blocks.argtypes = [P(Shape), ctypes.c_int32, P(Records), vp, vp]
         l.hkv_token_drift.argtypes = [vp, vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
                                       ctypes.c_int32, vp, vp]
-        l.hkv_select_top_tokens.argtypes = [vp, ctypes.c_int32, ctypes.c_int32, vp, vp]
+        l.hkv_select_top_tokens.argtypes = [vp, ctypes.c_int32, ctypes.c_int32, vp, vp,
+                                            ctypes.c_int64, vp]
+        l.hkv_select_workspace_bytes.argtypes = [ctypes.c_int32]
+        l.hkv_select_workspace_bytes.restype = ctypes.c_int64
         l.hkv_frame_headers.argtypes = [P(Shape), ctypes.c_int32, P(Records), vp, vp,
                                         ctypes.c_int32, vp]
         l.hkv_frame_verify.argtypes = [P(Shape), ctypes.c_int32, P(Records), ctypes.c_int32,
@@ -320,8 +323,15 @@ def token_drift(h_cached, h_fresh, out=None, stream=None):
     return out
 
 
-def select_top_tokens(drift, k: int, out=None, stream=None):
-    """Indices of the k largest drift values, increasing; int32 tensor [k]."""
+def select_workspace_bytes(n_tokens: int) -> int:
+    return int(lib().hkv_select_workspace_bytes(int(n_tokens)))
+
+
+def select_top_tokens(drift, k: int, out=None, workspace=True, stream=None):
+    """Indices of the k largest drift values, increasing; int32 tensor [k].
+    workspace: True (a device buffer of select_workspace_bytes is allocated
+    here: the many-workgroup path), None/False (one workgroup), or a uint8
+    tensor to use as the workspace."""
     if drift.dtype != torch.float32 or not drift.is_contiguous():
         raise ValueError("drift must be a contiguous float32 tensor")
     n = drift.numel()
@@ -329,8 +339,17 @@ def select_top_tokens(drift, k: int, out=None, stream=None):
         out = torch.empty(max(int(k), 0), dtype=torch.int32, device=drift.device)
     if out.numel() < k:
         raise ValueError("out must hold k entries")
+    if workspace is True:
+        workspace = torch.empty(max(select_workspace_bytes(n), 16), dtype=torch.uint8,
+                                device=drift.device)
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None and workspace is not False:
+        if workspace.dtype != torch.uint8 or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous uint8 tensor")
+        ws_ptr, ws_bytes = ctypes.c_void_p(workspace.data_ptr()), workspace.numel()
     st = lib().hkv_select_top_tokens(ctypes.c_void_p(drift.data_ptr()), n, int(k),
-                                     _i32(out, "out"), _stream(stream, drift.device))
+                                     _i32(out, "out"), ws_ptr, ws_bytes,
+                                     _stream(stream, drift.device))
     _check("hkv_select_top_tokens", st)
     return out
 

@@ -17,7 +17,7 @@ def test_exports_every_declared_symbol():
                           "hkv_page_visit_order", "hkv_fetch_dequant_rope_shift_tokens",
                           "hkv_stream_pair_create", "hkv_stream_destroy", "hkv_token_drift",
                           "hkv_select_top_tokens", "hkv_frame_headers", "hkv_frame_verify",
-                          "hkv_frame_delta_m"}
+                          "hkv_frame_delta_m", "hkv_select_workspace_bytes"}
     lib = H.lib()
     for n in names:
         assert getattr(lib, n) is not None
@@ -217,8 +217,8 @@ def test_drift_rejects_bad_arguments(name, kw):
 
 def test_select_rejects_bad_arguments():
     lib = H.lib()
-    call = lambda d=FAKE, n=100, k=15, o=FAKE + 4096: lib.hkv_select_top_tokens(
-        ctypes.c_void_p(d), n, k, ctypes.c_void_p(o), None)
+    call = lambda d=FAKE, n=100, k=15, o=FAKE + 4096, ws=None, wsb=0: lib.hkv_select_top_tokens(
+        ctypes.c_void_p(d), n, k, ctypes.c_void_p(o), ctypes.c_void_p(ws), wsb, None)
     assert call(k=101) == H.ERR_INVALID_ARG
     assert call(k=-1) == H.ERR_INVALID_ARG
     assert call(n=-1, k=0) == H.ERR_INVALID_ARG
@@ -226,6 +226,10 @@ def test_select_rejects_bad_arguments():
     assert call(o=0) == H.ERR_INVALID_ARG
     assert call(d=FAKE + 2) == H.ERR_INVALID_ARG
     assert call(k=0, d=0, o=0) == H.OK               # empty: nothing launched
+    need = H.select_workspace_bytes(100)
+    assert call(ws=FAKE + 8192, wsb=need - 4) == H.ERR_INVALID_ARG      # too small
+    assert call(ws=FAKE + 8200, wsb=need) == H.ERR_INVALID_ARG          # misaligned
+    assert call(n=(1 << 30) + 1, k=1) == H.ERR_UNSUPPORTED
     assert _drift(n=0, a=0, b=0, out=0) == H.OK
     # one row: the stride is not used; zero width: the rows are not read
     assert _drift(n=1, stride=0, a=0) == H.ERR_INVALID_ARG
@@ -289,3 +293,13 @@ def test_frame_allocation_shapes():
     fr4 = H.alloc_frames(1, 2, "int4", 1, 1, device="cpu")
     assert fr4.shape[2] == 64 + 132 and fr4.stride(1) == 256
     assert fr.dtype == torch.uint8
+
+
+def test_select_workspace_sizes():
+    ws = H.select_workspace_bytes
+    assert ws(-1) == -1 and ws((1 << 30) + 1) == -1
+    assert ws(0) == 4 * 8
+    assert ws(1) == 4 * (1 * (3 * 2048 + 2) + 8)
+    assert ws(65536) == 4 * (16 * (3 * 2048 + 2) + 8)
+    assert ws(65537) == 4 * (33 * (3 * 2048 + 2) + 8)      # 33 slices of 2,048 tokens
+    assert ws(1 << 30) == 4 * (64 * (3 * 2048 + 2) + 8)

@@ -140,29 +140,49 @@ SELECT_CASES = [
 ]
 
 
+PATHS = [True, None]                     # many workgroups with a workspace; one workgroup
+
+
+@pytest.mark.parametrize("ws", PATHS, ids=["workspace", "one_group"])
 @pytest.mark.parametrize("name,values,k", SELECT_CASES, ids=[c[0] for c in SELECT_CASES])
-def test_selection_edge_cases(name, values, k):
-    print(f"[select] {name} n={values.size} k={k}", flush=True)
+def test_selection_edge_cases(name, values, k, ws):
+    print(f"[select] {name} n={values.size} k={k} workspace={ws}", flush=True)
     d = torch.from_numpy(values).to(DEV)
-    sel = hkv.select_top_tokens(d, k)
+    sel = hkv.select_top_tokens(d, k, workspace=ws)
     torch.cuda.synchronize()
     assert np.array_equal(sel.cpu().numpy(), O.select_top_tokens(values, k)), name
 
 
-def test_selection_large_random_and_empty():
+@pytest.mark.parametrize("ws", PATHS, ids=["workspace", "one_group"])
+def test_selection_large_random_and_empty(ws):
     rng = np.random.default_rng(8)
     n = 300_000
     v = (np.abs(rng.standard_normal(n)) * 4).astype(np.float16).astype(np.float32)  # many ties
     d = torch.from_numpy(v).to(DEV)
     for k in (1, 45_000, n - 1):
-        print(f"[select] large n={n} k={k}", flush=True)
-        sel = hkv.select_top_tokens(d, k)
+        print(f"[select] large n={n} k={k} workspace={ws}", flush=True)
+        sel = hkv.select_top_tokens(d, k, workspace=ws)
         torch.cuda.synchronize()
         assert np.array_equal(sel.cpu().numpy(), O.select_top_tokens(v, k))
     out = torch.full((4,), -7, dtype=torch.int32, device=DEV)
-    hkv.select_top_tokens(d, 0, out=out)
+    hkv.select_top_tokens(d, 0, out=out, workspace=ws)
     torch.cuda.synchronize()
     assert out.cpu().tolist() == [-7] * 4             # k = 0 writes nothing
+
+
+def test_selection_workspace_reused_across_sizes():
+    # one workspace sized for the largest call serves smaller ones after it,
+    # across the slice-size change at 65,536 tokens and ragged last slices
+    rng = np.random.default_rng(9)
+    ws = torch.empty(hkv.select_workspace_bytes(200_003), dtype=torch.uint8, device=DEV)
+    for n in (200_003, 65_537, 65_536, 4_097, 4_096, 1_000, 1):
+        v = rng.standard_normal(n).astype(np.float32)
+        v[rng.integers(0, n, n // 10)] = 0.5                # ties
+        k = max(1, (n * 15) // 100)
+        print(f"[select] reused workspace n={n} k={k}", flush=True)
+        sel = hkv.select_top_tokens(torch.from_numpy(v).to(DEV), k, workspace=ws)
+        torch.cuda.synchronize()
+        assert np.array_equal(sel.cpu().numpy(), O.select_top_tokens(v, k)), n
 
 
 def test_side_stream_selection_matches():
@@ -192,10 +212,12 @@ def test_full_size_drift_and_selection(w):
     drift = hkv.token_drift(c, f)
     k = O.recompute_count(w.n_tokens)
     sel = hkv.select_top_tokens(drift, k)
+    sel1 = hkv.select_top_tokens(drift, k, workspace=None)
     torch.cuda.synchronize()
     dg = drift.cpu().numpy()
     s = sel.cpu().numpy()
     assert np.array_equal(s, O.select_top_tokens(dg, k))
+    assert np.array_equal(sel1.cpu().numpy(), s)
     assert not dg[:w.lead_tokens].any() and (dg[w.lead_tokens:] > 0).all()
     rng = np.random.default_rng(90)
     starts = w.lead_tokens + w.chunk_tokens * np.arange(w.n_chunks)

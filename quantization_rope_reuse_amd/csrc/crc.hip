@@ -11,7 +11,7 @@
 //   raw(A || B) = raw(A) * x^(8|B|) mod P  xor  raw(B),
 // and the standard CRC is ~(0xFFFFFFFF * x^(8|M|) mod P  xor  raw(M)).
 // One wave handles one record: lane i feeds its contiguous chunk of
-// `chunk` bytes into a zero register with a slicing-by-4 table in LDS, then
+// `chunk` bytes into a zero register, a word per three table lookups, then
 // the 64 lane values are merged pairwise in 6 rounds, round k shifting the
 // left half by x^(8 * chunk * 2^k).  Leading zero bytes leave a zero
 // register unchanged, so a record shorter than 64 * chunk is handled by
@@ -50,27 +50,55 @@ __device__ __forceinline__ uint32_t gf2_mulmod(uint32_t a, uint32_t b) {
   return p;
 }
 
-__device__ __forceinline__ uint32_t feed_word(const uint32_t (*T)[256], uint32_t c, uint32_t w) {
+// Feeding a little-endian word w into the register is c <- A(c ^ w), with A
+// the linear map "shift through 32 zero bits".  A splits over the bit
+// fields [0, 11), [11, 22) and [22, 32) of its argument, so one word costs
+// three lookups in the tables T0[v] = A(v), T1[v] = A(v << 11),
+// T2[v] = A(v << 22) (2,048 + 2,048 + 1,024 entries in LDS).
+__device__ __forceinline__ uint32_t feed_word(const uint32_t* T0, const uint32_t* T1,
+                                              const uint32_t* T2, uint32_t c, uint32_t w) {
   c ^= w;
-  return T[3][c & 0xFFu] ^ T[2][(c >> 8) & 0xFFu] ^ T[1][(c >> 16) & 0xFFu] ^ T[0][c >> 24];
+  return T0[c & 0x7FFu] ^ T1[(c >> 11) & 0x7FFu] ^ T2[c >> 22];
+}
+
+// A(1 << k), k = 0..31, by 32 bit steps.
+__device__ __forceinline__ uint32_t shift32(uint32_t x) {
+#pragma unroll
+  for (int k = 0; k < 32; ++k) x = (x >> 1) ^ (kPoly & (0u - (x & 1u)));
+  return x;
+}
+
+// Builds T0 | T1 | T2 (5,120 words) in LDS with 256 threads: the 32 basis
+// values A(1 << k) first, then each thread fills runs of 8 consecutive
+// entries, entry v0 + t being the run's first entry xor the basis
+// combination of t.
+__device__ __forceinline__ void build_tables(uint32_t* T, uint32_t* basis, int tid) {
+  if (tid < 32) basis[tid] = shift32(1u << tid);
+  __syncthreads();
+  for (int run = tid; run < 5120 / 8; run += kThreads) {
+    const int e0 = run * 8;                      // first entry of the run
+    const int off = e0 < 2048 ? 0 : (e0 < 4096 ? 11 : 22);
+    const int v0 = e0 - (off == 0 ? 0 : (off == 11 ? 2048 : 4096));
+    uint32_t head = 0;
+    const int bits = off == 22 ? 10 : 11;
+    for (int j = 3; j < bits; ++j)
+      if ((v0 >> j) & 1) head ^= basis[off + j];
+    const uint32_t b0 = basis[off], b1 = basis[off + 1], b2 = basis[off + 2];
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+      T[e0 + t] = head ^ ((t & 1) ? b0 : 0u) ^ ((t & 2) ? b1 : 0u) ^ ((t & 4) ? b2 : 0u);
+  }
+  __syncthreads();
 }
 
 __global__ __launch_bounds__(kThreads) void crc32_kernel(CrcParams p) {
-  __shared__ uint32_t T[4][256];
+  __shared__ uint32_t T[5120];
+  __shared__ uint32_t basis[32];
   const int tid = threadIdx.x;
-  {
-    uint32_t c = static_cast<uint32_t>(tid);
-#pragma unroll
-    for (int k = 0; k < 8; ++k) c = (c >> 1) ^ (kPoly & (0u - (c & 1u)));
-    T[0][tid] = c;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int s = 1; s < 4; ++s) {
-    const uint32_t prev = T[s - 1][tid];
-    T[s][tid] = (prev >> 8) ^ T[0][prev & 0xFFu];
-    __syncthreads();
-  }
+  build_tables(T, basis, tid);
+  const uint32_t* T0 = T;
+  const uint32_t* T1 = T + 2048;
+  const uint32_t* T2 = T + 4096;
 
   const int lane = tid & (kWave - 1);
   const int r = blockIdx.x * kRecordsPerGroup + tid / kWave;
@@ -90,23 +118,23 @@ __global__ __launch_bounds__(kThreads) void crc32_kernel(CrcParams p) {
       for (int j = 0; j < 8; ++j) w[j] = *reinterpret_cast<const u32x4*>(base + u + 16 * j);
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        crc = feed_word(T, crc, w[j][0]);
-        crc = feed_word(T, crc, w[j][1]);
-        crc = feed_word(T, crc, w[j][2]);
-        crc = feed_word(T, crc, w[j][3]);
+        crc = feed_word(T0, T1, T2, crc, w[j][0]);
+        crc = feed_word(T0, T1, T2, crc, w[j][1]);
+        crc = feed_word(T0, T1, T2, crc, w[j][2]);
+        crc = feed_word(T0, T1, T2, crc, w[j][3]);
       }
     }
     for (; u < p.chunk; u += 16) {
       const u32x4 w = *reinterpret_cast<const u32x4*>(base + u);
-      crc = feed_word(T, crc, w[0]);
-      crc = feed_word(T, crc, w[1]);
-      crc = feed_word(T, crc, w[2]);
-      crc = feed_word(T, crc, w[3]);
+      crc = feed_word(T0, T1, T2, crc, w[0]);
+      crc = feed_word(T0, T1, T2, crc, w[1]);
+      crc = feed_word(T0, T1, T2, crc, w[2]);
+      crc = feed_word(T0, T1, T2, crc, w[3]);
     }
   } else {
     const uint8_t* base = rec + start;
     for (; u < p.chunk; u += 4)
-      crc = feed_word(T, crc, *reinterpret_cast<const uint32_t*>(base + u));
+      crc = feed_word(T0, T1, T2, crc, *reinterpret_cast<const uint32_t*>(base + u));
   }
 
 #pragma unroll

@@ -239,6 +239,7 @@ def main():
 
     frames = frames_leg(dev, hkv, W, w, L, src_k, src_v, put_tab)
     select = recompute_select(dev, hkv, W)
+    others = other_workloads(dev, hkv, W)
 
     if a.calibrate_copy:
         # torch.neg over 2**28 fp32 values: reads exactly 1 GiB, writes 1 GiB
@@ -303,11 +304,73 @@ def main():
                 "gbps": round(put_bytes / (float(np.mean(put_ms)) * 1e-3) / 1e9, 1)},
         "crc32": {"mean_ms_incl_stream_handoff": round(float(np.mean(crc_ms)), 4),
                   "gbps": round(crc_bytes / (float(np.mean(crc_ms)) * 1e-3) / 1e9, 1)},
+        "other_workloads": others,
         "frames": frames,
         "recompute_select": select,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
+
+
+def other_workloads(dev, hkv, W, reps=5):
+    """Put and fetch throughput on the Qwen3-8B-shaped (FP8, fp16 pages, random
+    per-block deltas) and INT4 disk-tier (fp16 with outlier channels) caches,
+    all layers in one call per operation.  Outside the step; HIP events."""
+    import numpy as np
+    import torch
+    res = {}
+    for w, fmt in ((W.QWEN3_8B, "fp8"), (W.INT4_L3, "int4")):
+        L, nb, tb, H = w.n_layers, w.n_blocks, w.block_tokens, w.n_kv_heads
+        dt = {"f16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32}[w.src_dtype]
+        src_k = torch.empty((L, nb, tb, H, 128), dtype=dt, device=dev)
+        src_v = torch.empty_like(src_k)
+        put_tab = torch.from_numpy(W.put_table(w)).to(dev)
+        tmp = torch.empty((w.n_tokens, H, 128), dtype=torch.float32, device=dev)
+        gen = torch.Generator(device=dev)
+        for l in range(L):
+            for kv, dst in ((0, src_k), (1, src_v)):
+                W.device_layer_values(w, l, kv, tmp, generator=gen)
+                dst[l].index_copy_(0, put_tab.long(), tmp.view(nb, tb, H, 128).to(dt))
+        del tmp
+        rec = hkv.alloc_records(L, nb, fmt, tb, H, device=dev)
+        ftab = torch.from_numpy(W.fetch_table(w)).to(dev)
+        dm = torch.from_numpy(W.delta_m(w)).to(dev)
+        order = hkv.page_visit_order(ftab, nb)
+        out_k = torch.empty_like(src_k)
+        out_v = torch.empty_like(src_k)
+        put = hkv.quant_fp8 if fmt == "fp8" else hkv.quant_int4
+        s = torch.cuda.current_stream(dev)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        put_ms, fetch_ms = [], []
+        for rep in range(reps + 1):
+            ev[0].record(s)
+            put(src_k, src_v, put_tab, rec, stream=s)
+            ev[1].record(s)
+            hkv.fetch_dequant_rope_shift(rec, fmt, ftab, dm, w.rope_base, w.pairs, out_k, out_v,
+                                         visit_order=order, stream=s)
+            ev[2].record(s)
+            s.synchronize()
+            if rep:
+                put_ms.append(ev[0].elapsed_time(ev[1]))
+                fetch_ms.append(ev[1].elapsed_time(ev[2]))
+        cb = 128 if fmt == "fp8" else 64
+        vecs = 2 * L * w.n_tokens * H
+        es = src_k.element_size()
+        fetch_bytes = vecs * (cb + 2 + 128 * es) + L * nb * 8
+        put_bytes = vecs * (128 * es + cb + 2) + L * nb * 4
+        fms, pms = float(np.mean(fetch_ms)), float(np.mean(put_ms))
+        res[w.name] = {
+            "format": fmt,
+            "fetch_ms": round(fms, 4),
+            "fetch_gbps": round(fetch_bytes / (fms * 1e-3) / 1e9, 1),
+            "fetch_frac_of_peak": round(fetch_bytes / (fms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+            "fetch_tokens_per_s": round(w.n_tokens / (fms * 1e-3), 0),
+            "put_ms": round(pms, 4),
+            "put_gbps": round(put_bytes / (pms * 1e-3) / 1e9, 1),
+        }
+        del src_k, src_v, rec, out_k, out_v
+        torch.cuda.empty_cache()
+    return res
 
 
 def frames_leg(dev, hkv, W, w, L, src_k, src_v, put_tab, reps=3):

@@ -130,13 +130,18 @@ __device__ __forceinline__ uint32_t quant_vector(float (&a)[8], float (&b)[8], u
     __builtin_nontemporal_store(f32x8_to_fp8(a), reinterpret_cast<u32x2*>(c_ptr + 8 * sub));
     __builtin_nontemporal_store(f32x8_to_fp8(b), reinterpret_cast<u32x2*>(c_ptr + 64 + 8 * sub));
   } else {
+    // q clamped to [-7, 7] (integers, so clamping before rounding is the
+    // same as after), then 1.5 * 2^23 added: the fp32 sum has unit spacing
+    // there, so the addition itself rounds q to the nearest integer, ties
+    // to even, and the low four bits of the sum are that integer in two's
+    // complement -- the nibble.
     uint32_t wa = 0, wb = 0;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const int ia = static_cast<int>(__builtin_amdgcn_fmed3f(rintf(a[j]), -7.0f, 7.0f));
-      const int ib = static_cast<int>(__builtin_amdgcn_fmed3f(rintf(b[j]), -7.0f, 7.0f));
-      wa |= (static_cast<uint32_t>(ia) & 0xFu) << (4 * j);
-      wb |= (static_cast<uint32_t>(ib) & 0xFu) << (4 * j);
+      const float ra = __builtin_amdgcn_fmed3f(a[j], -7.0f, 7.0f) + 12582912.0f;
+      const float rb = __builtin_amdgcn_fmed3f(b[j], -7.0f, 7.0f) + 12582912.0f;
+      wa |= (__builtin_bit_cast(uint32_t, ra) & 0xFu) << (4 * j);
+      wb |= (__builtin_bit_cast(uint32_t, rb) & 0xFu) << (4 * j);
     }
     __builtin_nontemporal_store(wa, reinterpret_cast<uint32_t*>(c_ptr + 4 * sub));
     __builtin_nontemporal_store(wb, reinterpret_cast<uint32_t*>(c_ptr + 32 + 4 * sub));

@@ -11,7 +11,16 @@
  *   fetch  dequantize, rotate every key pair by the block's position delta
  *          dm = m_new - m_old, leave values unrotated, and scatter into a
  *          paged KV buffer through a block table
- *          (hkv_fetch_dequant_rope_shift).
+ *          (hkv_fetch_dequant_rope_shift; one delta per token:
+ *          hkv_fetch_dequant_rope_shift_tokens; a destination-ordered visit
+ *          list: hkv_page_visit_order);
+ *   frame  a self-describing header in front of each record, its
+ *          verification, and dm from the stored position (hkv_frame_*);
+ *   select the tokens to recompute after a chunk reorder: per-token drift
+ *          of the layer-0 hidden state and the top k (hkv_token_drift,
+ *          hkv_select_top_tokens);
+ *   overlap two compute-unit-partitioned streams for a fetch running beside
+ *          compute (hkv_stream_pair_create).
  *
  * The operations follow two web pages:
  *   "HyperCache – Distributed KV-cache quantization and relative RoPE reuse"
@@ -29,8 +38,9 @@
  * - All array pointers are DEVICE pointers owned by the caller; the structs
  *   themselves are read from host memory during the call only.
  * - Calls are asynchronous on `stream` (0 = the default stream), allocate
- *   no memory, keep no state between calls and may be called from several
- *   host threads at once.
+ *   no memory (hkv_stream_pair_create aside, which creates two streams),
+ *   keep no state between calls and may be called from several host
+ *   threads at once.
  * - Return value: HKV_OK (0) or a negative hkv_status.  Argument errors are
  *   detected on the host before anything is launched; nothing throws across
  *   the ABI.  A launch failure is reported as HKV_ERR_HIP.

@@ -232,6 +232,26 @@ def main():
         side.synchronize()
     tok_ms = ev_t[0].elapsed_time(ev_t[1])
 
+    # the 80 per-layer fetch launches captured once in a HIP graph and replayed
+    graph = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        for l in range(L):
+            hkv.fetch_dequant_rope_shift(rec_l[l], "fp8", ftab, dm, w.rope_base, w.pairs,
+                                         ok_l[l], ov_l[l], visit_order=order)
+    torch.cuda.synchronize()
+    ev_g = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    cur = torch.cuda.current_stream(dev)
+    graph_ms = []
+    for rep in range(4):
+        ev_g[0].record(cur)
+        graph.replay()
+        ev_g[1].record(cur)
+        cur.synchronize()
+        if rep:
+            graph_ms.append(ev_g[0].elapsed_time(ev_g[1]))
+    del graph
+
     if a.overlap:
         print(json.dumps(overlap(a, w, L, hkv, rec_l, ok_l, ov_l, ftab, dm, order, side)),
               flush=True)
@@ -299,6 +319,11 @@ def main():
             "gbps": round(fetch_bytes / (tok_ms * 1e-3) / 1e9, 1),
             "ms_80_layers": round(tok_ms, 4),
             "note": "hkv_fetch_dequant_rope_shift_tokens, one delta per token",
+        },
+        "fetch_graph": {
+            "ms_80_layers": round(float(np.mean(graph_ms)), 4),
+            "gbps": round(fetch_bytes / (float(np.mean(graph_ms)) * 1e-3) / 1e9, 1),
+            "note": "the same 80 per-layer launches captured once in a HIP graph, replayed",
         },
         "put": {"mean_ms": round(float(np.mean(put_ms)), 4),
                 "gbps": round(put_bytes / (float(np.mean(put_ms)) * 1e-3) / 1e9, 1)},

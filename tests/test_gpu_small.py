@@ -172,6 +172,36 @@ def test_ragged_shapes_skips_and_strides(fmt, src_dtype, out_dtype):
                 assert canary_k[:, p].all(), f"page {p} was written"
 
 
+@pytest.mark.parametrize("fmt", ["fp8", "int4"])
+def test_large_blocks(fmt):
+    """Blocks of 1,024 tokens x 16 heads (16,384 vectors, 256 workgroups per
+    block and K|V; a 4.3 MB FP8 record, one CRC wave per record with 66 KB
+    lane chunks): put, CRC and fetch against the oracle."""
+    rng = np.random.default_rng(67)
+    L, P, tb, H = 1, 2, 1024, 16
+    print(f"[small] large blocks {fmt}", flush=True)
+    kp = rng.standard_normal((L, P, tb, H, 128)).astype(np.float32)
+    vp = rng.standard_normal((L, P, tb, H, 128)).astype(np.float32)
+    table = np.array([1, 0], dtype=np.int32)
+    rec, ref, live = _put_both(kp, vp, table, fmt, "bf16")
+    assert np.array_equal(rec.cpu().numpy(), ref)
+    crc = hkv.crc32_blocks(rec, fmt, tb, H)
+    assert np.array_equal(crc_u32(crc), O.crc32_records(ref))
+    dm = np.array([-123457, 65535], dtype=np.int32)
+    ko = canary_fill(torch.empty((L, P, tb, H, 128), dtype=torch.float16, device=DEV))
+    vo = canary_fill(torch.empty_like(ko))
+    hkv.fetch_dequant_rope_shift(rec, fmt, _dev_i32(table), _dev_i32(dm), 500000.0,
+                                 "half_split", ko, vo)
+    torch.cuda.synchronize()
+    kr, vd = O.fetch_exact(ref, fmt, tb, H, dm, 500000.0, "half_split")
+    kd, _ = O.dequant_records(ref, fmt, tb, H)
+    kg, vg = host_f64(ko), host_f64(vo)
+    for b in range(2):
+        page = int(table[b])
+        compare_fetch_block(kg[:, page], vg[:, page], kr[:, b], vd[:, b], kd[:, b], "f16",
+                            int(dm[b]), f"large block {b}")
+
+
 def test_scale_edge_cases_fp32_source():
     """All-zero vectors (with signed zeros), scales that underflow or
     overflow fp16, and saturation beyond 448."""

@@ -6,9 +6,10 @@ RoPE base 500000 with split-halves pairs, every block re-used 8,192 positions
 later.  Synthetic standard-normal values drawn on the GPU.
 
 One step is one pass of the whole hot path over that cache:
-  1. put    FP8 E4M3 quantization of all 80 layers, gathered through a
-            permuted block table into per-(layer, block) records (10.9 GB);
-  2. CRC-32 of every record;
+  1+2. put and CRC  FP8 E4M3 quantization of all 80 layers, gathered through a
+            permuted block table into per-(layer, block) records (10.9 GB),
+            with the CRC-32 of every record computed in the same pass
+            (hkv_quant_fp8_crc: one put launch + a small merge launch);
   3. fetch  layer by layer on a side stream (80 launches): dequantize, shift
             keys by +8192, scatter into a second paged bf16 buffer through
             another permuted table, visiting blocks in destination-page order
@@ -23,12 +24,15 @@ Reported (one JSON line on stdout):
                measured with rocprofv3 counters for the current fetch source,
                else null
   fetch        fetch-only GB/s, fraction of peak, tokens/s
+  put_crc      the fused put + CRC phase; put, crc32: the same work as two
+               separate passes, timed outside the step
   cpu_baseline the CPU oracle on a bounded sample of the same workload
 
-Algorithmic bytes (what the method must move):
+Algorithmic bytes (what each step of the method covers):
   put    per vector 128 * 2 (bf16 read) + 128 + 2 (codes and scale written),
          plus the 4-byte table entry per (layer, block);
-  CRC    per record its bytes read plus 4 written;
+  CRC    per record its bytes plus 4 written (counted as the bytes the CRC
+         covers; in the fused pass they come from LDS, not a second read);
   fetch  per vector 128 + 2 read + 128 * 2 written, plus the 4-byte table
          entry and 4-byte delta per (layer, block).
 """
@@ -142,6 +146,8 @@ def main():
     del tmp
     records = hkv.alloc_records(L, nb, "fp8", tb, H, device=dev)
     crc = torch.empty((L, nb), dtype=torch.int32, device=dev)
+    crc_ws = torch.empty(hkv.quant_crc_workspace_bytes("fp8", L, nb, tb, H), dtype=torch.uint8,
+                         device=dev)
     order = torch.empty(nb, dtype=torch.int32, device=dev)
     out_k = torch.empty_like(src_k)
     out_v = torch.empty_like(src_k)
@@ -161,10 +167,12 @@ def main():
         # per-layer fetch launches, which would add a gap between them)
         if ev is not None:
             ev[0].record(main_stream)
-        hkv.quant_fp8(src_k, src_v, put_tab, records, stream=main_stream)
+        # put and CRC in one pass (the put stages each workgroup's codes in
+        # LDS and writes per-128-byte raw CRCs; a small kernel merges them)
+        hkv.quant_crc("fp8", src_k, src_v, put_tab, records, crc_out=crc, workspace=crc_ws,
+                      stream=main_stream)
         if ev is not None:
             ev[1].record(main_stream)
-        hkv.crc32_blocks(records, "fp8", tb, H, out=crc, stream=main_stream)
         ready = torch.cuda.Event()
         ready.record(main_stream)
         side.wait_event(ready)
@@ -197,8 +205,7 @@ def main():
     elapsed = time.perf_counter() - t0
     ms_per_step = elapsed * 1e3 / a.steps
 
-    put_ms = [e[0].elapsed_time(e[1]) for e in events]
-    crc_ms = [e[1].elapsed_time(e[2]) for e in events]        # includes the stream hand-off
+    put_crc_ms = [e[0].elapsed_time(e[1]) for e in events]
     fetch_span_ms = [e[2].elapsed_time(e[3]) for e in events]
     fetch_ms = [f / L for f in fetch_span_ms]                  # mean per launch
 
@@ -257,6 +264,8 @@ def main():
               flush=True)
         return
 
+    separate = separate_put_crc(dev, hkv, L, nb, tb, H, src_k, src_v, put_tab, records, crc,
+                                put_bytes, crc_bytes)
     frames = frames_leg(dev, hkv, W, w, L, src_k, src_v, put_tab)
     select = recompute_select(dev, hkv, W)
     others = other_workloads(dev, hkv, W)
@@ -290,8 +299,9 @@ def main():
         "data": "synthetic N(0,1), generated on the GPU",
         "config": {
             "workload": "Llama-3-70B-shaped KV, one GPU: 80 layers x 8 KV heads x d128 x "
-                        "65536 tokens bf16, blocks of 64, FP8 put + CRC32 + layer-by-layer "
-                        "fetch on a side stream, dm=+8192, RoPE base 500000 split-halves",
+                        "65536 tokens bf16, blocks of 64, FP8 put + CRC32 in one pass + "
+                        "layer-by-layer fetch on a side stream, dm=+8192, RoPE base 500000 "
+                        "split-halves",
             "layers": L, "tokens": T, "kv_heads": H, "head_dim": 128, "block_tokens": tb,
             "step_bytes": step_bytes,
         },
@@ -325,16 +335,49 @@ def main():
             "gbps": round(fetch_bytes / (float(np.mean(graph_ms)) * 1e-3) / 1e9, 1),
             "note": "the same 80 per-layer launches captured once in a HIP graph, replayed",
         },
-        "put": {"mean_ms": round(float(np.mean(put_ms)), 4),
-                "gbps": round(put_bytes / (float(np.mean(put_ms)) * 1e-3) / 1e9, 1)},
-        "crc32": {"mean_ms_incl_stream_handoff": round(float(np.mean(crc_ms)), 4),
-                  "gbps": round(crc_bytes / (float(np.mean(crc_ms)) * 1e-3) / 1e9, 1)},
+        "put_crc": {"mean_ms": round(float(np.mean(put_crc_ms)), 4),
+                    "gbps": round((put_bytes + crc_bytes) / (float(np.mean(put_crc_ms)) * 1e-3)
+                                  / 1e9, 1),
+                    "note": "hkv_quant_fp8_crc: put and CRC-32 in one pass (the step's "
+                            "phase); CRC bytes counted as the record bytes it covers"},
+        "put": separate["put"],
+        "crc32": separate["crc32"],
         "other_workloads": others,
         "frames": frames,
         "recompute_select": select,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
+
+
+def separate_put_crc(dev, hkv, L, nb, tb, H, src_k, src_v, put_tab, records, crc, put_bytes,
+                     crc_bytes, reps=5):
+    """The put (hkv_quant_fp8) and the CRC (hkv_crc32_blocks) as two passes over
+    the same cache, each timed with HIP events on the current stream; their
+    CRCs must equal the fused pass's from the step."""
+    import numpy as np
+    import torch
+    s = torch.cuda.current_stream(dev)
+    crc2 = torch.empty_like(crc)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    put_ms, crc_ms = [], []
+    for rep in range(reps + 1):
+        ev[0].record(s)
+        hkv.quant_fp8(src_k, src_v, put_tab, records, stream=s)
+        ev[1].record(s)
+        hkv.crc32_blocks(records, "fp8", tb, H, out=crc2, stream=s)
+        ev[2].record(s)
+        s.synchronize()
+        if rep:
+            put_ms.append(ev[0].elapsed_time(ev[1]))
+            crc_ms.append(ev[1].elapsed_time(ev[2]))
+    if not torch.equal(crc, crc2):
+        raise RuntimeError("the CRC kernel disagrees with the fused put + CRC")
+    pm, cm = float(np.mean(put_ms)), float(np.mean(crc_ms))
+    return {"put": {"mean_ms": round(pm, 4), "gbps": round(put_bytes / (pm * 1e-3) / 1e9, 1),
+                    "note": "hkv_quant_fp8 alone"},
+            "crc32": {"mean_ms": round(cm, 4), "gbps": round(crc_bytes / (cm * 1e-3) / 1e9, 1),
+                      "note": "hkv_crc32_blocks alone (records read back)"}}
 
 
 def other_workloads(dev, hkv, W, reps=5):
@@ -409,6 +452,8 @@ def frames_leg(dev, hkv, W, w, L, src_k, src_v, put_tab, reps=3):
     frames = hkv.alloc_frames(L, nb, "fp8", tb, H, device=dev)
     rec = hkv.frame_records(frames)
     crc = torch.empty((L, nb), dtype=torch.int32, device=dev)
+    crc_ws = torch.empty(hkv.quant_crc_workspace_bytes("fp8", L, nb, tb, H), dtype=torch.uint8,
+                         device=dev)
     flags = torch.empty((L, nb), dtype=torch.int32, device=dev)
     m_old = torch.from_numpy(W.block_positions(w)[0]).to(dev)
     s = torch.cuda.current_stream(dev)

@@ -7,7 +7,8 @@
  *   put    quantize post-RoPE K and V head vectors of 128 elements to FP8
  *          E4M3 or to INT4, one fp16 scale per vector (hkv_quant_fp8,
  *          hkv_quant_int4);
- *   check  CRC-32 of each record (hkv_crc32_blocks);
+ *   check  CRC-32 of each record (hkv_crc32_blocks; fused with the put:
+ *          hkv_quant_fp8_crc, hkv_quant_int4_crc);
  *   fetch  dequantize, rotate every key pair by the block's position delta
  *          dm = m_new - m_old, leave values unrotated, and scatter into a
  *          paged KV buffer through a block table
@@ -139,6 +140,29 @@ int hkv_quant_fp8(const hkv_shape* shape, const hkv_pages* src, int32_t src_dtyp
 int hkv_quant_int4(const hkv_shape* shape, const hkv_pages* src, int32_t src_dtype,
                    const int32_t* block_table, const hkv_records* dst,
                    hipStream_t stream);
+
+/* Put and CRC in one pass (HyperCache post: Part B, the L3-disk line: INT4
+ * records written with their CRC32).  Writes the same records as
+ * hkv_quant_fp8 / hkv_quant_int4 and to crc_out (uint32 [n_layers *
+ * n_blocks], device, layer-major) the CRC-32 of every record the put wrote,
+ * equal to what hkv_crc32_blocks computes over them; entries of skipped
+ * blocks are left unchanged.  The put kernel stages each workgroup's codes
+ * and scales in LDS and stores the raw CRC of every 128-byte unit of the
+ * record to `workspace`; a second kernel merges them per record.
+ * workspace: 16-byte aligned device memory of at least
+ * hkv_quant_crc_workspace_bytes() bytes (4 bytes per 128 bytes of records);
+ * when block_tokens * n_kv_heads is not a multiple of 64 that is 0, no
+ * workspace is needed and the call runs the put and then the CRC kernel. */
+int hkv_quant_fp8_crc(const hkv_shape* shape, const hkv_pages* src, int32_t src_dtype,
+                      const int32_t* block_table, const hkv_records* dst, uint32_t* crc_out,
+                      void* workspace, int64_t workspace_bytes, hipStream_t stream);
+int hkv_quant_int4_crc(const hkv_shape* shape, const hkv_pages* src, int32_t src_dtype,
+                       const int32_t* block_table, const hkv_records* dst, uint32_t* crc_out,
+                       void* workspace, int64_t workspace_bytes, hipStream_t stream);
+
+/* Workspace bytes for hkv_quant_*_crc with this shape and format; -1 on bad
+ * arguments. */
+int64_t hkv_quant_crc_workspace_bytes(const hkv_shape* shape, int32_t fmt);
 
 /* Fetch (HyperCache post: Core Design, relative-RoPE paragraph; Part B, the
  * socket-fetch line with RoPE applied on the fly).

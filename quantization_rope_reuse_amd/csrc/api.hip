@@ -129,6 +129,44 @@ int quant_common(int32_t fmt, const hkv_shape* shape, const hkv_pages* src, int3
   return to_status(hkv::launch_quant(fmt, src_dtype, g, pv, block_table, rv, stream));
 }
 
+int64_t quant_crc_workspace(const Geometry& g, int64_t rb) {
+  if (g.vecs % 64 != 0) return 0;                 // runs the put and the CRC kernel
+  return static_cast<int64_t>(g.n_layers) * g.n_blocks * (rb / 128) * 4;
+}
+
+int quant_crc_common(int32_t fmt, const hkv_shape* shape, const hkv_pages* src,
+                     int32_t src_dtype, const int32_t* block_table, const hkv_records* dst,
+                     uint32_t* crc_out, void* workspace, int64_t workspace_bytes,
+                     hipStream_t stream) {
+  Geometry g;
+  PageView pv;
+  RecordView rv;
+  int st;
+  if ((st = check_shape(shape, &g)) != HKV_OK) return st;
+  if ((st = check_pages(src, src_dtype, &pv)) != HKV_OK) return st;
+  if ((st = check_records(dst, fmt, shape, &rv)) != HKV_OK) return st;
+  if (!block_table && g.n_blocks > 0) return HKV_ERR_INVALID_ARG;
+  if (!crc_out && g.n_layers > 0 && g.n_blocks > 0) return HKV_ERR_INVALID_ARG;
+  const int64_t rb = hkv_record_bytes(fmt, shape->block_tokens, shape->n_kv_heads,
+                                      shape->head_dim);
+  if (rb > (int64_t{1} << 30)) return HKV_ERR_UNSUPPORTED;
+  const int64_t need = quant_crc_workspace(g, rb);
+  if (need > 0 && (!workspace || !aligned16(workspace) || workspace_bytes < need))
+    return HKV_ERR_INVALID_ARG;
+  if (g.n_layers == 0 || g.n_blocks == 0) return HKV_OK;
+  if (need == 0) {
+    const hipError_t e = hkv::launch_quant(fmt, src_dtype, g, pv, block_table, rv, stream);
+    if (e != hipSuccess) return HKV_ERR_HIP;
+    return to_status(hkv::launch_crc32(g, rb, rv, crc_out, stream));
+  }
+  uint32_t* partials = static_cast<uint32_t*>(workspace);
+  const hipError_t e = hkv::launch_quant_crc_units(fmt, src_dtype, g, pv, block_table, rv, rb,
+                                                   partials, stream);
+  if (e != hipSuccess) return HKV_ERR_HIP;
+  return to_status(hkv::launch_crc32_merge(g, rb, block_table, pv.num_pages, partials, crc_out,
+                                           stream));
+}
+
 int fetch_common(const hkv_shape* shape, int32_t fmt, const hkv_records* src,
                  const int32_t* block_table, const int32_t* delta_m, bool per_token,
                  const int32_t* visit_order, double rope_base, int32_t pairs,
@@ -182,6 +220,28 @@ int hkv_quant_int4(const hkv_shape* shape, const hkv_pages* src, int32_t src_dty
   return quant_common(HKV_INT4, shape, src, src_dtype, block_table, dst, stream);
 }
 
+
+int64_t hkv_quant_crc_workspace_bytes(const hkv_shape* shape, int32_t fmt) {
+  Geometry g;
+  if (!valid_format(fmt) || check_shape(shape, &g) != HKV_OK) return -1;
+  const int64_t rb = hkv_record_bytes(fmt, shape->block_tokens, shape->n_kv_heads,
+                                      shape->head_dim);
+  return quant_crc_workspace(g, rb);
+}
+
+int hkv_quant_fp8_crc(const hkv_shape* shape, const hkv_pages* src, int32_t src_dtype,
+                      const int32_t* block_table, const hkv_records* dst, uint32_t* crc_out,
+                      void* workspace, int64_t workspace_bytes, hipStream_t stream) {
+  return quant_crc_common(HKV_FP8_E4M3, shape, src, src_dtype, block_table, dst, crc_out,
+                          workspace, workspace_bytes, stream);
+}
+
+int hkv_quant_int4_crc(const hkv_shape* shape, const hkv_pages* src, int32_t src_dtype,
+                       const int32_t* block_table, const hkv_records* dst, uint32_t* crc_out,
+                       void* workspace, int64_t workspace_bytes, hipStream_t stream) {
+  return quant_crc_common(HKV_INT4, shape, src, src_dtype, block_table, dst, crc_out,
+                          workspace, workspace_bytes, stream);
+}
 
 int hkv_fetch_dequant_rope_shift(const hkv_shape* shape, int32_t fmt, const hkv_records* src,
                                  const int32_t* block_table, const int32_t* delta_m,

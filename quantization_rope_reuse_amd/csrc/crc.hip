@@ -148,6 +148,56 @@ __global__ __launch_bounds__(kThreads) void crc32_kernel(CrcParams p) {
   if (lane == 0) p.out[r] = ~(p.init_term ^ crc);
 }
 
+// Merge of the fused put + CRC: `partials` holds, for every record, the raw
+// CRC of each of its `units` 128-byte units (record bytes / 128, written by
+// the put).  Lane i takes units i, i+64, i+128, ... (leading zero units pad
+// the count to a multiple of 64) and advances c <- c * x^(8*128*64) xor
+// raw(unit), the constant multiplication being four lookups in a table built
+// per workgroup; the 64 lane values merge with shifts x^(8 * 128 * 2^k).
+// Records of skipped blocks (table entry negative or >= num_pages) are left
+// alone.
+struct MergeParams {
+  const uint32_t* partials;
+  const int32_t* table;
+  uint32_t* out;
+  int32_t n_blocks, n_records, num_pages;
+  int32_t units, pad, per_lane;
+  uint32_t mul_lanes;        // x^(8 * 128 * 64) mod P
+  uint32_t shift[6];         // x^(8 * 128 * 2^k) mod P
+  uint32_t init_term;        // 0xFFFFFFFF * x^(8 * record bytes) mod P
+};
+
+__global__ __launch_bounds__(kThreads) void crc32_merge_kernel(MergeParams p) {
+  __shared__ uint32_t M[4][256];                 // M[k][b] = (b at byte k) * mul_lanes
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+    M[k][tid] = gf2_mulmod(static_cast<uint32_t>(tid) << (8 * k), p.mul_lanes);
+  __syncthreads();
+  const int lane = tid & (kWave - 1);
+  const int r = blockIdx.x * kRecordsPerGroup + tid / kWave;
+  if (r >= p.n_records) return;                 // whole wave, after the barrier
+  const int blk = r % p.n_blocks;
+  const int page = p.table[blk];
+  if (page < 0 || page >= p.num_pages) return;
+  const uint32_t* part = p.partials + static_cast<int64_t>(r) * p.units;
+  uint32_t c = 0;
+  for (int j = 0; j < p.per_lane; ++j) {
+    const int u = lane + kWave * j - p.pad;
+    const uint32_t w = u >= 0 ? part[u] : 0u;
+    c = M[0][c & 0xFFu] ^ M[1][(c >> 8) & 0xFFu] ^ M[2][(c >> 16) & 0xFFu] ^ M[3][c >> 24] ^ w;
+  }
+#pragma unroll
+  for (int k = 0; k < 6; ++k) {
+    const uint32_t other = __shfl_xor(c, 1 << k);
+    const bool left = ((lane >> k) & 1) == 0;
+    const uint32_t lo = left ? c : other;       // earlier bytes
+    const uint32_t hi = left ? other : c;
+    c = gf2_mulmod(lo, p.shift[k]) ^ hi;
+  }
+  if (lane == 0) p.out[r] = ~(p.init_term ^ c);
+}
+
 // Host side: the same GF(2) arithmetic for the launch constants.
 uint32_t host_mulmod(uint32_t a, uint32_t b) {
   uint32_t prod = 0;
@@ -196,6 +246,29 @@ hipError_t launch_crc32(const Geometry& g, int64_t record_bytes, const RecordVie
   const unsigned groups =
       static_cast<unsigned>((p.n_records + kRecordsPerGroup - 1) / kRecordsPerGroup);
   hipLaunchKernelGGL(crc32_kernel, dim3(groups), dim3(kThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_crc32_merge(const Geometry& g, int64_t record_bytes, const int32_t* table,
+                              int32_t num_pages, const uint32_t* partials, uint32_t* out,
+                              hipStream_t stream) {
+  MergeParams p;
+  p.partials = partials;
+  p.table = table;
+  p.out = out;
+  p.n_blocks = g.n_blocks;
+  p.n_records = g.n_layers * g.n_blocks;
+  p.num_pages = num_pages;
+  const int64_t units = record_bytes / 128;
+  p.units = static_cast<int32_t>(units);
+  p.pad = static_cast<int32_t>((kWave - units % kWave) % kWave);
+  p.per_lane = static_cast<int32_t>((units + p.pad) / kWave);
+  p.mul_lanes = host_x8n(static_cast<uint64_t>(128) * kWave);
+  for (int k = 0; k < 6; ++k) p.shift[k] = host_x8n(static_cast<uint64_t>(128) << k);
+  p.init_term = host_mulmod(0xFFFFFFFFu, host_x8n(static_cast<uint64_t>(record_bytes)));
+  const unsigned groups =
+      static_cast<unsigned>((p.n_records + kRecordsPerGroup - 1) / kRecordsPerGroup);
+  hipLaunchKernelGGL(crc32_merge_kernel, dim3(groups), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -27,13 +27,40 @@ struct QuantParams {
   int64_t s_layer, s_page, s_token, s_head;
   int32_t num_pages;
   const int32_t* table;
+  int32_t table_blocks;  // n_blocks (records per layer)
   uint8_t* rec;
   int64_t rec_layer, rec_block;
   int32_t n_heads;
   int32_t vecs;
   int32_t chunks;
   int32_t vecs_per_chunk;
+  uint32_t* partials;    // fused CRC: raw CRC of every 128-byte unit of every record
+  int32_t units;         // 128-byte units per record
 };
+
+// CRC-32 byte tables (zlib polynomial, reflected), slicing by four: T[0] is
+// the one-byte table and T[s][i] feeds T[s-1][i] one more zero byte.
+// Built by the 256 threads of the workgroup; ends with a barrier.
+__device__ __forceinline__ void build_crc_tables(uint32_t (*T)[256]) {
+  const int tid = threadIdx.x;
+  uint32_t c = static_cast<uint32_t>(tid);
+#pragma unroll
+  for (int k = 0; k < 8; ++k) c = (c >> 1) ^ (0xEDB88320u & (0u - (c & 1u)));
+  T[0][tid] = c;
+  __syncthreads();
+#pragma unroll
+  for (int s = 1; s < 4; ++s) {
+    const uint32_t prev = T[s - 1][tid];
+    T[s][tid] = (prev >> 8) ^ T[0][prev & 0xFFu];
+    __syncthreads();
+  }
+}
+
+__device__ __forceinline__ uint32_t crc_feed_word(const uint32_t (*T)[256], uint32_t c,
+                                                  uint32_t w) {
+  c ^= w;
+  return T[3][c & 0xFFu] ^ T[2][(c >> 8) & 0xFFu] ^ T[1][(c >> 16) & 0xFFu] ^ T[0][c >> 24];
+}
 
 // fp16 bits of the scale for a vector with max magnitude amax (fp32).
 // Edge cases: amax == 0 -> 0; a positive amax whose scale underflows fp16 ->
@@ -97,9 +124,10 @@ __device__ __forceinline__ float div_by_scale(float x, float s, float r) {
 
 // Quantize one vector's lane-owned runs a (elements 8s..8s+7) and b
 // (64+8s..64+8s+7); returns the fp16 scale bits (same in all 8 lanes).
-template <int FMT>
+// STAGE: the code bytes also go to `stage` (LDS) at the same offsets.
+template <int FMT, bool STAGE>
 __device__ __forceinline__ uint32_t quant_vector(float (&a)[8], float (&b)[8], uint8_t* c_ptr,
-                                                 int sub, bool active) {
+                                                 int sub, bool active, uint8_t* stage) {
   // |x| compared as integers: for finite values the magnitude bits order
   // exactly like the magnitudes.
   uint32_t mbits = 0;
@@ -127,8 +155,14 @@ __device__ __forceinline__ uint32_t quant_vector(float (&a)[8], float (&b)[8], u
       a[j] = __builtin_amdgcn_fmed3f(a[j], -448.0f, 448.0f);
       b[j] = __builtin_amdgcn_fmed3f(b[j], -448.0f, 448.0f);
     }
-    __builtin_nontemporal_store(f32x8_to_fp8(a), reinterpret_cast<u32x2*>(c_ptr + 8 * sub));
-    __builtin_nontemporal_store(f32x8_to_fp8(b), reinterpret_cast<u32x2*>(c_ptr + 64 + 8 * sub));
+    const u32x2 ca = f32x8_to_fp8(a);
+    const u32x2 cb = f32x8_to_fp8(b);
+    __builtin_nontemporal_store(ca, reinterpret_cast<u32x2*>(c_ptr + 8 * sub));
+    __builtin_nontemporal_store(cb, reinterpret_cast<u32x2*>(c_ptr + 64 + 8 * sub));
+    if constexpr (STAGE) {
+      *reinterpret_cast<u32x2*>(stage + 8 * sub) = ca;
+      *reinterpret_cast<u32x2*>(stage + 64 + 8 * sub) = cb;
+    }
   } else {
     // q clamped to [-7, 7] (integers, so clamping before rounding is the
     // same as after), then 1.5 * 2^23 added: the fp32 sum has unit spacing
@@ -145,6 +179,10 @@ __device__ __forceinline__ uint32_t quant_vector(float (&a)[8], float (&b)[8], u
     }
     __builtin_nontemporal_store(wa, reinterpret_cast<uint32_t*>(c_ptr + 4 * sub));
     __builtin_nontemporal_store(wb, reinterpret_cast<uint32_t*>(c_ptr + 32 + 4 * sub));
+    if constexpr (STAGE) {
+      *reinterpret_cast<uint32_t*>(stage + 4 * sub) = wa;
+      *reinterpret_cast<uint32_t*>(stage + 32 + 4 * sub) = wb;
+    }
   }
   return sbits;
 }
@@ -156,7 +194,15 @@ __device__ __forceinline__ uint32_t quant_vector(float (&a)[8], float (&b)[8], u
 // cannot be waited for without also waiting for the store.  Lane L collects
 // the scale of vector v0 + L and stores it once at the end.  Record stores
 // are non-temporal.
-template <int FMT, int SDT>
+//
+// CRC (fused put + CRC-32, chunks of exactly kQuantGroupVecs vectors): the
+// workgroup's codes form a contiguous run of the record (8 KB FP8, 4 KB
+// INT4) and its 64 scales another one (128 B); both are staged in LDS as they
+// are written, and after a barrier one thread per 128-byte unit feeds its
+// unit into a zero CRC register (byte tables in LDS) and stores that raw
+// value in `partials` at the unit's index in the record.  A second kernel
+// merges the units of each record (crc.hip).
+template <int FMT, int SDT, bool CRC>
 __global__ __launch_bounds__(kThreads) void quant_kernel(QuantParams p) {
   const int layer = blockIdx.y;
   const int chunk = blockIdx.x % p.chunks;
@@ -164,7 +210,13 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(QuantParams p) {
   const int kv = bk & 1;
   const int blk = bk >> 1;
   const int page = p.table[blk];
-  if (page < 0 || page >= p.num_pages) return;
+  if (page < 0 || page >= p.num_pages) return;   // uniform over the workgroup
+
+  constexpr int kCB = FMT == kFP8 ? kHeadDim : kHeadDim / 2;
+  __shared__ __align__(16) uint8_t stage[CRC ? kQuantGroupVecs * kCB : 16];
+  __shared__ __align__(16) uint16_t stage_scales[CRC ? kQuantGroupVecs : 8];
+  __shared__ uint32_t T[CRC ? 4 : 1][256];
+  if constexpr (CRC) build_crc_tables(T);
 
   constexpr int CB = FMT == kFP8 ? kHeadDim : kHeadDim / 2;
   constexpr int ES = ElemSize<SDT>::value;
@@ -180,8 +232,9 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(QuantParams p) {
   const int sub = lane & (kLanesPerVec - 1);
   const int vsub = lane / kLanesPerVec;
   const int v_end = min((chunk + 1) * p.vecs_per_chunk, p.vecs);
-  const int v0 = chunk * p.vecs_per_chunk + wave * kWaveVecs;
-  if (v0 >= v_end) return;                      // whole wave idle
+  const int chunk_v0 = chunk * p.vecs_per_chunk;
+  const int v0 = chunk_v0 + wave * kWaveVecs;
+  if (!CRC && v0 >= v_end) return;              // whole wave idle (never with CRC)
 
   uint32_t my_scale = 0;
 #pragma unroll
@@ -210,37 +263,60 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(QuantParams p) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) a[j] = b[j] = 0.0f;
       }
-      const uint32_t sbits = quant_vector<FMT>(a, b, codes + static_cast<int64_t>(v) * CB, sub,
-                                               active);
+      const uint32_t sbits = quant_vector<FMT, CRC>(a, b, codes + static_cast<int64_t>(v) * CB,
+                                                    sub, active, stage + (v - chunk_v0) * CB);
       // lane 8*(i0+i) + r keeps the scale of vector r of this pass
       const uint32_t got = __shfl(sbits, (lane & 7) * kLanesPerVec);
       if (lane / kLanesPerVec == i0 + i) my_scale = got;
     }
   }
-  if (lane < kWaveVecs && v0 + lane < v_end) scales[v0 + lane] = static_cast<uint16_t>(my_scale);
-}
-
-template <int FMT, int SDT>
-hipError_t launch_t(const QuantParams& p, const Geometry& g, hipStream_t stream) {
-  dim3 grid(static_cast<unsigned>(g.n_blocks) * 2u * static_cast<unsigned>(p.chunks),
-            static_cast<unsigned>(g.n_layers));
-  hipLaunchKernelGGL((quant_kernel<FMT, SDT>), grid, dim3(kThreads), 0, stream, p);
-  return hipGetLastError();
-}
-
-template <int FMT>
-hipError_t launch_dtype(int sdt, const QuantParams& p, const Geometry& g, hipStream_t s) {
-  switch (sdt) {
-    case kF32: return launch_t<FMT, kF32>(p, g, s);
-    case kF16: return launch_t<FMT, kF16>(p, g, s);
-    default: return launch_t<FMT, kBF16>(p, g, s);
+  if (lane < kWaveVecs && v0 + lane < v_end) {
+    scales[v0 + lane] = static_cast<uint16_t>(my_scale);
+    if constexpr (CRC) stage_scales[v0 - chunk_v0 + lane] = static_cast<uint16_t>(my_scale);
+  }
+  if constexpr (CRC) {
+    __syncthreads();
+    constexpr int kCodeUnits = kQuantGroupVecs * CB / 128;
+    const int u = threadIdx.x;
+    if (u <= kCodeUnits) {                          // kCodeUnits: the scale unit
+      const u32x4* w = u < kCodeUnits ? reinterpret_cast<const u32x4*>(stage + u * 128)
+                                      : reinterpret_cast<const u32x4*>(stage_scales);
+      uint32_t c = 0;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const u32x4 x = w[q];
+        c = crc_feed_word(T, c, x[0]);
+        c = crc_feed_word(T, c, x[1]);
+        c = crc_feed_word(T, c, x[2]);
+        c = crc_feed_word(T, c, x[3]);
+      }
+      const int64_t byte = u < kCodeUnits
+          ? static_cast<int64_t>(kv) * p.vecs * CB + static_cast<int64_t>(chunk_v0) * CB + u * 128
+          : 2LL * p.vecs * CB + 2LL * kv * p.vecs + 2LL * chunk_v0;
+      p.partials[(static_cast<int64_t>(layer) * (p.table_blocks) + blk) * p.units + byte / 128] = c;
+    }
   }
 }
 
-}  // namespace
+template <int FMT, int SDT, bool CRC>
+hipError_t launch_t(const QuantParams& p, const Geometry& g, hipStream_t stream) {
+  dim3 grid(static_cast<unsigned>(g.n_blocks) * 2u * static_cast<unsigned>(p.chunks),
+            static_cast<unsigned>(g.n_layers));
+  hipLaunchKernelGGL((quant_kernel<FMT, SDT, CRC>), grid, dim3(kThreads), 0, stream, p);
+  return hipGetLastError();
+}
 
-hipError_t launch_quant(int fmt, int src_dtype, const Geometry& g, const PageView& src,
-                        const int32_t* table, const RecordView& dst, hipStream_t stream) {
+template <int FMT, bool CRC>
+hipError_t launch_dtype(int sdt, const QuantParams& p, const Geometry& g, hipStream_t s) {
+  switch (sdt) {
+    case kF32: return launch_t<FMT, kF32, CRC>(p, g, s);
+    case kF16: return launch_t<FMT, kF16, CRC>(p, g, s);
+    default: return launch_t<FMT, kBF16, CRC>(p, g, s);
+  }
+}
+
+QuantParams make_params(const Geometry& g, const PageView& src, const int32_t* table,
+                        const RecordView& dst) {
   QuantParams p;
   p.k_src = src.k;
   p.v_src = src.v;
@@ -250,6 +326,7 @@ hipError_t launch_quant(int fmt, int src_dtype, const Geometry& g, const PageVie
   p.s_head = src.head;
   p.num_pages = src.num_pages;
   p.table = table;
+  p.table_blocks = g.n_blocks;
   p.rec = dst.base;
   p.rec_layer = dst.layer;
   p.rec_block = dst.block;
@@ -257,8 +334,28 @@ hipError_t launch_quant(int fmt, int src_dtype, const Geometry& g, const PageVie
   p.vecs = g.vecs;
   p.chunks = (g.vecs + kQuantGroupVecs - 1) / kQuantGroupVecs;
   p.vecs_per_chunk = kQuantGroupVecs;
-  return fmt == kFP8 ? launch_dtype<kFP8>(src_dtype, p, g, stream)
-                     : launch_dtype<kINT4>(src_dtype, p, g, stream);
+  p.partials = nullptr;
+  p.units = 0;
+  return p;
+}
+
+}  // namespace
+
+hipError_t launch_quant(int fmt, int src_dtype, const Geometry& g, const PageView& src,
+                        const int32_t* table, const RecordView& dst, hipStream_t stream) {
+  const QuantParams p = make_params(g, src, table, dst);
+  return fmt == kFP8 ? launch_dtype<kFP8, false>(src_dtype, p, g, stream)
+                     : launch_dtype<kINT4, false>(src_dtype, p, g, stream);
+}
+
+hipError_t launch_quant_crc_units(int fmt, int src_dtype, const Geometry& g, const PageView& src,
+                                  const int32_t* table, const RecordView& dst,
+                                  int64_t record_bytes, uint32_t* partials, hipStream_t stream) {
+  QuantParams p = make_params(g, src, table, dst);
+  p.partials = partials;
+  p.units = static_cast<int32_t>(record_bytes / 128);
+  return fmt == kFP8 ? launch_dtype<kFP8, true>(src_dtype, p, g, stream)
+                     : launch_dtype<kINT4, true>(src_dtype, p, g, stream);
 }
 
 }  // namespace hkv

@@ -79,6 +79,11 @@ def lib():
         vp = ctypes.c_void_p
         l.hkv_quant_fp8.argtypes = [P(Shape), P(Pages), ctypes.c_int32, vp, P(Records), vp]
         l.hkv_quant_int4.argtypes = [P(Shape), P(Pages), ctypes.c_int32, vp, P(Records), vp]
+        l.hkv_quant_fp8_crc.argtypes = [P(Shape), P(Pages), ctypes.c_int32, vp, P(Records), vp,
+                                        vp, ctypes.c_int64, vp]
+        l.hkv_quant_int4_crc.argtypes = l.hkv_quant_fp8_crc.argtypes
+        l.hkv_quant_crc_workspace_bytes.argtypes = [P(Shape), ctypes.c_int32]
+        l.hkv_quant_crc_workspace_bytes.restype = ctypes.c_int64
         l.hkv_fetch_dequant_rope_shift.argtypes = [
             P(Shape), ctypes.c_int32, P(Records), vp, vp, vp, ctypes.c_double, ctypes.c_int32,
             P(Pages), ctypes.c_int32, vp]
@@ -102,7 +107,8 @@ def lib():
         l.hkv_stream_pair_create.restype = ctypes.c_int
         l.hkv_stream_destroy.argtypes = [vp]
         l.hkv_stream_destroy.restype = ctypes.c_int
-        for name in ("hkv_quant_fp8", "hkv_quant_int4", "hkv_fetch_dequant_rope_shift",
+        for name in ("hkv_quant_fp8", "hkv_quant_int4", "hkv_quant_fp8_crc",
+                     "hkv_quant_int4_crc", "hkv_fetch_dequant_rope_shift",
                      "hkv_fetch_dequant_rope_shift_tokens", "hkv_crc32_blocks",
                      "hkv_page_visit_order", "hkv_token_drift", "hkv_select_top_tokens",
                      "hkv_frame_headers", "hkv_frame_verify", "hkv_frame_delta_m"):
@@ -210,6 +216,44 @@ def quant_fp8(k_pages, v_pages, block_table, records, stream=None):
 def quant_int4(k_pages, v_pages, block_table, records, stream=None):
     """Quantize the blocks k/v_pages[:, block_table[b]] into records[:, b] (INT4)."""
     return _quant("hkv_quant_int4", k_pages, v_pages, block_table, records, stream)
+
+
+def quant_crc_workspace_bytes(fmt, n_layers: int, n_blocks: int, block_tokens: int,
+                              n_kv_heads: int) -> int:
+    shape = Shape(n_layers, n_blocks, block_tokens, n_kv_heads, HEAD_DIM)
+    return int(lib().hkv_quant_crc_workspace_bytes(ctypes.byref(shape), FORMATS[fmt]))
+
+
+def quant_crc(fmt, k_pages, v_pages, block_table, records, crc_out=None, workspace=True,
+              stream=None):
+    """Put (FP8 or INT4) and the CRC-32 of every written record in one pass.
+    Returns crc_out, an int32 tensor [L, n_blocks] holding uint32 values.
+    workspace: True (allocated here), or a uint8 tensor of at least
+    quant_crc_workspace_bytes bytes."""
+    pages, shp, dt = _pages(k_pages, v_pages)
+    L, _, tb, H, d = shp
+    nb = block_table.numel()
+    if records.shape[0] != L or records.shape[1] != nb:
+        raise ValueError("records must be [L, n_blocks, bytes] matching pages and table")
+    if crc_out is None:
+        crc_out = torch.empty((L, nb), dtype=torch.int32, device=records.device)
+    if crc_out.dtype != torch.int32 or not crc_out.is_contiguous() or crc_out.numel() != L * nb:
+        raise ValueError("crc_out must be a contiguous int32 tensor of L * n_blocks elements")
+    need = quant_crc_workspace_bytes(fmt, L, nb, tb, H)
+    if workspace is True:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=records.device)
+    if workspace.dtype != torch.uint8 or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous uint8 tensor")
+    shape = Shape(L, nb, tb, H, d)
+    rec = _records(records)
+    name = "hkv_quant_fp8_crc" if FORMATS[fmt] == FP8_E4M3 else "hkv_quant_int4_crc"
+    st = getattr(lib(), name)(ctypes.byref(shape), ctypes.byref(pages), dt,
+                              _i32(block_table, "block_table"), ctypes.byref(rec),
+                              ctypes.c_void_p(crc_out.data_ptr()),
+                              ctypes.c_void_p(workspace.data_ptr()), workspace.numel(),
+                              _stream(stream, k_pages.device))
+    _check(name, st)
+    return crc_out
 
 
 def _fetch(name, records, fmt, block_table, delta, n_delta, rope_base, pairs, k_pages, v_pages,

@@ -17,7 +17,9 @@ def test_exports_every_declared_symbol():
                           "hkv_page_visit_order", "hkv_fetch_dequant_rope_shift_tokens",
                           "hkv_stream_pair_create", "hkv_stream_destroy", "hkv_token_drift",
                           "hkv_select_top_tokens", "hkv_frame_headers", "hkv_frame_verify",
-                          "hkv_frame_delta_m", "hkv_select_workspace_bytes"}
+                          "hkv_frame_delta_m", "hkv_select_workspace_bytes",
+                          "hkv_quant_fp8_crc", "hkv_quant_int4_crc",
+                          "hkv_quant_crc_workspace_bytes"}
     lib = H.lib()
     for n in names:
         assert getattr(lib, n) is not None
@@ -303,3 +305,23 @@ def test_select_workspace_sizes():
     assert ws(65536) == 4 * (16 * (3 * 2048 + 2) + 8)
     assert ws(65537) == 4 * (33 * (3 * 2048 + 2) + 8)      # 33 slices of 2,048 tokens
     assert ws(1 << 30) == 4 * (64 * (3 * 2048 + 2) + 8)
+
+
+def test_fused_put_crc_rejects_bad_arguments():
+    lib = H.lib()
+    s, p, r = _shape(), _pages(), _recs()           # 16 x 8 = 128 vectors: fused path
+    need = lib.hkv_quant_crc_workspace_bytes(ctypes.byref(s), 0)
+    assert need == 2 * 4 * (33280 // 128) * 4
+    assert lib.hkv_quant_crc_workspace_bytes(ctypes.byref(_shape(head_dim=64)), 0) == -1
+    assert lib.hkv_quant_crc_workspace_bytes(ctypes.byref(s), 9) == -1
+    # 5 x 3 = 15 vectors: no workspace (put, then the CRC kernel)
+    assert lib.hkv_quant_crc_workspace_bytes(ctypes.byref(_shape(block_tokens=5, n_kv_heads=3)),
+                                             1) == 0
+    call = lambda crc=FAKE, ws=FAKE + 4096, wsb=need, sh=s: lib.hkv_quant_fp8_crc(
+        ctypes.byref(sh), ctypes.byref(p), 0, ctypes.c_void_p(FAKE), ctypes.byref(r),
+        ctypes.c_void_p(crc), ctypes.c_void_p(ws), wsb, None)
+    assert call(crc=0) == H.ERR_INVALID_ARG
+    assert call(ws=0) == H.ERR_INVALID_ARG
+    assert call(wsb=need - 1) == H.ERR_INVALID_ARG
+    assert call(ws=FAKE + 4100) == H.ERR_INVALID_ARG               # misaligned
+    assert call(sh=_shape(n_blocks=0), crc=0, ws=0, wsb=0) == H.OK

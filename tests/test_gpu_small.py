@@ -202,6 +202,38 @@ def test_large_blocks(fmt):
                             int(dm[b]), f"large block {b}")
 
 
+@pytest.mark.parametrize("fmt", ["fp8", "int4"])
+@pytest.mark.parametrize("shape", [(16, 8, 2, 5), (64, 8, 1, 3), (37, 9, 2, 4), (8, 16, 3, 6)],
+                         ids=["16x8", "64x8", "37x9_fallback", "8x16"])
+def test_fused_put_crc(fmt, shape):
+    """Put and CRC in one pass: the records equal the separate put's, the CRCs
+    equal the oracle's for every written block, and the entries of skipped
+    blocks stay as they were.  37 x 9 = 333 vectors per block is not a
+    multiple of 64: that shape runs the put and the CRC kernel."""
+    tb, H, L, P = shape
+    print(f"[small] fused put+crc {fmt} {shape}", flush=True)
+    rng = np.random.default_rng(71)
+    kp = rng.standard_normal((L, P, tb, H, 128)).astype(np.float32)
+    vp = (rng.standard_normal((L, P, tb, H, 128)) * 5).astype(np.float32)
+    table = np.array(([P - 1, -1] + list(range(P - 1)) + [P + 7])[:P + 2], dtype=np.int32)
+    rec, ref, live = _put_both(kp, vp, table, fmt, "bf16")
+    kt = torch.from_numpy(kp).to(DEV, torch.bfloat16)
+    vt = torch.from_numpy(vp).to(DEV, torch.bfloat16)
+    rec2 = hkv.alloc_records(L, len(table), fmt, tb, H, device=DEV)
+    rec2.fill_(0xA5)
+    crc = torch.full((L, len(table)), 0x1234567, dtype=torch.int32, device=DEV)
+    hkv.quant_crc(fmt, kt, vt, _dev_i32(table), rec2, crc_out=crc)
+    torch.cuda.synchronize()
+    assert torch.equal(rec2, rec), "fused put wrote different records"
+    got = crc_u32(crc)
+    want = O.crc32_records(ref)
+    for b in range(len(table)):
+        if live[b]:
+            assert np.array_equal(got[:, b], want[:, b]), f"block {b} CRC"
+        elif tb * H % 64 == 0:
+            assert (got[:, b] == 0x1234567).all(), f"skipped block {b} CRC was written"
+
+
 def test_scale_edge_cases_fp32_source():
     """All-zero vectors (with signed zeros), scales that underflow or
     overflow fp16, and saturation beyond 448."""

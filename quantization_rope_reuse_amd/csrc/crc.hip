@@ -17,13 +17,13 @@
 // register unchanged, so a record shorter than 64 * chunk is handled by
 // treating it as preceded by `pad` zero bytes.  The shift constants depend
 // only on the record size and are computed once per launch on the host.
+#include "crc_device.h"
 #include "hkv_device.h"
 #include "hkv_launch.h"
 
 namespace hkv {
 namespace {
 
-constexpr uint32_t kPoly = 0xEDB88320u;   // reflected x^32 + x^26 + ... + 1
 constexpr int kRecordsPerGroup = kThreads / kWave;
 
 struct CrcParams {
@@ -39,17 +39,6 @@ struct CrcParams {
   uint32_t init_term;    // 0xFFFFFFFF * x^(8 * record bytes) mod P
 };
 
-// a * b mod P in the reflected representation (bit 31 holds x^0).
-__device__ __forceinline__ uint32_t gf2_mulmod(uint32_t a, uint32_t b) {
-  uint32_t p = 0;
-#pragma unroll
-  for (int j = 0; j < 32; ++j) {
-    p ^= b & (0u - ((a >> (31 - j)) & 1u));
-    b = (b >> 1) ^ (kPoly & (0u - (b & 1u)));
-  }
-  return p;
-}
-
 // Feeding a little-endian word w into the register is c <- A(c ^ w), with A
 // the linear map "shift through 32 zero bits".  A splits over the bit
 // fields [0, 11), [11, 22) and [22, 32) of its argument, so one word costs
@@ -64,7 +53,7 @@ __device__ __forceinline__ uint32_t feed_word(const uint32_t* T0, const uint32_t
 // A(1 << k), k = 0..31, by 32 bit steps.
 __device__ __forceinline__ uint32_t shift32(uint32_t x) {
 #pragma unroll
-  for (int k = 0; k < 32; ++k) x = (x >> 1) ^ (kPoly & (0u - (x & 1u)));
+  for (int k = 0; k < 32; ++k) x = (x >> 1) ^ (kCrcPoly & (0u - (x & 1u)));
   return x;
 }
 
@@ -143,7 +132,7 @@ __global__ __launch_bounds__(kThreads) void crc32_kernel(CrcParams p) {
     const bool left = ((lane >> k) & 1) == 0;
     const uint32_t lo = left ? crc : other;     // earlier bytes
     const uint32_t hi = left ? other : crc;
-    crc = gf2_mulmod(lo, p.shift[k]) ^ hi;
+    crc = crc_mulmod(lo, p.shift[k]) ^ hi;
   }
   if (lane == 0) p.out[r] = ~(p.init_term ^ crc);
 }
@@ -172,7 +161,7 @@ __global__ __launch_bounds__(kThreads) void crc32_merge_kernel(MergeParams p) {
   const int tid = threadIdx.x;
 #pragma unroll
   for (int k = 0; k < 4; ++k)
-    M[k][tid] = gf2_mulmod(static_cast<uint32_t>(tid) << (8 * k), p.mul_lanes);
+    M[k][tid] = crc_mulmod(static_cast<uint32_t>(tid) << (8 * k), p.mul_lanes);
   __syncthreads();
   const int lane = tid & (kWave - 1);
   const int r = blockIdx.x * kRecordsPerGroup + tid / kWave;
@@ -193,31 +182,9 @@ __global__ __launch_bounds__(kThreads) void crc32_merge_kernel(MergeParams p) {
     const bool left = ((lane >> k) & 1) == 0;
     const uint32_t lo = left ? c : other;       // earlier bytes
     const uint32_t hi = left ? other : c;
-    c = gf2_mulmod(lo, p.shift[k]) ^ hi;
+    c = crc_mulmod(lo, p.shift[k]) ^ hi;
   }
   if (lane == 0) p.out[r] = ~(p.init_term ^ c);
-}
-
-// Host side: the same GF(2) arithmetic for the launch constants.
-uint32_t host_mulmod(uint32_t a, uint32_t b) {
-  uint32_t prod = 0;
-  for (int j = 0; j < 32; ++j) {
-    if (a & (0x80000000u >> j)) prod ^= b;
-    b = (b & 1u) ? (b >> 1) ^ kPoly : (b >> 1);
-  }
-  return prod;
-}
-
-// x^(8n) mod P, reflected.
-uint32_t host_x8n(uint64_t n) {
-  uint32_t result = 0x80000000u;   // x^0
-  uint32_t sq = 0x00800000u;       // x^8
-  while (n) {
-    if (n & 1u) result = host_mulmod(result, sq);
-    sq = host_mulmod(sq, sq);
-    n >>= 1;
-  }
-  return result;
 }
 
 }  // namespace
@@ -241,8 +208,8 @@ hipError_t launch_crc32(const Geometry& g, int64_t record_bytes, const RecordVie
   p.chunk = static_cast<int32_t>(chunk);
   p.pad = static_cast<int32_t>(kWave * chunk - record_bytes);
   p.aligned = aligned ? 1 : 0;
-  for (int k = 0; k < 6; ++k) p.shift[k] = host_x8n(static_cast<uint64_t>(chunk) << k);
-  p.init_term = host_mulmod(0xFFFFFFFFu, host_x8n(static_cast<uint64_t>(record_bytes)));
+  for (int k = 0; k < 6; ++k) p.shift[k] = crc_x8n(static_cast<uint64_t>(chunk) << k);
+  p.init_term = crc_mulmod(0xFFFFFFFFu, crc_x8n(static_cast<uint64_t>(record_bytes)));
   const unsigned groups =
       static_cast<unsigned>((p.n_records + kRecordsPerGroup - 1) / kRecordsPerGroup);
   hipLaunchKernelGGL(crc32_kernel, dim3(groups), dim3(kThreads), 0, stream, p);
@@ -263,9 +230,9 @@ hipError_t launch_crc32_merge(const Geometry& g, int64_t record_bytes, const int
   p.units = static_cast<int32_t>(units);
   p.pad = static_cast<int32_t>((kWave - units % kWave) % kWave);
   p.per_lane = static_cast<int32_t>((units + p.pad) / kWave);
-  p.mul_lanes = host_x8n(static_cast<uint64_t>(128) * kWave);
-  for (int k = 0; k < 6; ++k) p.shift[k] = host_x8n(static_cast<uint64_t>(128) << k);
-  p.init_term = host_mulmod(0xFFFFFFFFu, host_x8n(static_cast<uint64_t>(record_bytes)));
+  p.mul_lanes = crc_x8n(static_cast<uint64_t>(128) * kWave);
+  for (int k = 0; k < 6; ++k) p.shift[k] = crc_x8n(static_cast<uint64_t>(128) << k);
+  p.init_term = crc_mulmod(0xFFFFFFFFu, crc_x8n(static_cast<uint64_t>(record_bytes)));
   const unsigned groups =
       static_cast<unsigned>((p.n_records + kRecordsPerGroup - 1) / kRecordsPerGroup);
   hipLaunchKernelGGL(crc32_merge_kernel, dim3(groups), dim3(kThreads), 0, stream, p);

@@ -15,6 +15,7 @@
 // of kQuantGroupVecs vectors), kQuantPasses * 8 consecutive vectors per wave,
 // 8 lanes per vector; the vector's amax is reduced over its 8 lanes with
 // cross-lane max.
+#include "crc_device.h"
 #include "hkv_device.h"
 #include "hkv_launch.h"
 
@@ -37,30 +38,6 @@ struct QuantParams {
   uint32_t* partials;    // fused CRC: raw CRC of every 128-byte unit of every record
   int32_t units;         // 128-byte units per record
 };
-
-// CRC-32 byte tables (zlib polynomial, reflected), slicing by four: T[0] is
-// the one-byte table and T[s][i] feeds T[s-1][i] one more zero byte.
-// Built by the 256 threads of the workgroup; ends with a barrier.
-__device__ __forceinline__ void build_crc_tables(uint32_t (*T)[256]) {
-  const int tid = threadIdx.x;
-  uint32_t c = static_cast<uint32_t>(tid);
-#pragma unroll
-  for (int k = 0; k < 8; ++k) c = (c >> 1) ^ (0xEDB88320u & (0u - (c & 1u)));
-  T[0][tid] = c;
-  __syncthreads();
-#pragma unroll
-  for (int s = 1; s < 4; ++s) {
-    const uint32_t prev = T[s - 1][tid];
-    T[s][tid] = (prev >> 8) ^ T[0][prev & 0xFFu];
-    __syncthreads();
-  }
-}
-
-__device__ __forceinline__ uint32_t crc_feed_word(const uint32_t (*T)[256], uint32_t c,
-                                                  uint32_t w) {
-  c ^= w;
-  return T[3][c & 0xFFu] ^ T[2][(c >> 8) & 0xFFu] ^ T[1][(c >> 16) & 0xFFu] ^ T[0][c >> 24];
-}
 
 // fp16 bits of the scale for a vector with max magnitude amax (fp32).
 // Edge cases: amax == 0 -> 0; a positive amax whose scale underflows fp16 ->

@@ -2,7 +2,8 @@
 benchmark uses: the Qwen3-8B-shaped cache (36 layers, 32k tokens, fp16, one
 call per operation), the Llama-3-70B-shaped cache (80 layers, 64k tokens,
 bf16, fetch layer by layer on a side stream) and the INT4 disk-tier cache
-(32 layers, 16k tokens, fp16 with outlier channels, CRC tamper test).
+(32 layers, 16k tokens, fp16 with outlier channels, CRC tamper test, and the
+put and CRC in one pass against the two passes).
 
 The oracle cannot run over tens of gigabytes, so it runs on sampled blocks
 (seeded, plus the blocks with the extreme deltas and the first and last
@@ -136,8 +137,8 @@ def test_llama3_70b_full_layerwise_side_stream():
     src_k, src_v, put_tab = _fill_source(w)
     L, nb = w.n_layers, w.n_blocks
     rec = hkv.alloc_records(L, nb, "fp8", w.block_tokens, w.n_kv_heads, device=DEV)
-    hkv.quant_fp8(src_k, src_v, put_tab, rec)
-    crc = hkv.crc32_blocks(rec, "fp8", w.block_tokens, w.n_kv_heads)
+    # put and CRC in one pass, as the benchmark step runs them
+    crc = hkv.quant_crc("fp8", src_k, src_v, put_tab, rec)
     ftab = torch.from_numpy(W.fetch_table(w)).to(DEV)
     dm_np = W.delta_m(w)
     dm = torch.from_numpy(dm_np).to(DEV)
@@ -183,6 +184,13 @@ def test_int4_l3_full_with_tamper():
     # INT4 with outlier-dominated scales: a loose error bound, the parity above
     # is the pass criterion
     _properties(src_k, src_v, put_tab, out_k, out_v, ftab, rel_v=1.01, rel_norm=1.01)
+
+    # put and CRC in one pass: the same records and the same CRCs
+    rec2 = hkv.alloc_records(L, nb, "int4", w.block_tokens, w.n_kv_heads, device=DEV)
+    crc2 = hkv.quant_crc("int4", src_k, src_v, put_tab, rec2)
+    torch.cuda.synchronize()
+    assert torch.equal(rec2, rec) and torch.equal(crc2, crc)
+    del rec2
 
     # tamper detection: flip single bits / bytes in a few records; exactly
     # those records' CRCs change, to the oracle's CRC of the tampered bytes

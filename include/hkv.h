@@ -145,8 +145,10 @@ int hkv_quant_int4(const hkv_shape* shape, const hkv_pages* src, int32_t src_dty
  * records written with their CRC32).  Writes the same records as
  * hkv_quant_fp8 / hkv_quant_int4 and to crc_out (uint32 [n_layers *
  * n_blocks], device, layer-major) the CRC-32 of every record the put wrote,
- * equal to what hkv_crc32_blocks computes over them; entries of skipped
- * blocks are left unchanged.  The put kernel stages each workgroup's codes
+ * equal to what hkv_crc32_blocks computes over them.  Entries of skipped
+ * blocks are left unchanged by the one-pass path; the two-pass fallback
+ * (below) writes the CRC of whatever those records hold.  The put kernel
+ * stages each workgroup's codes
  * and scales in LDS and stores the raw CRC of every 128-byte unit of the
  * record to `workspace`; a second kernel merges them per record.
  * workspace: 16-byte aligned device memory of at least

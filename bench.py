@@ -26,6 +26,8 @@ Reported (one JSON line on stdout):
   fetch        fetch-only GB/s, fraction of peak, tokens/s
   put_crc      the fused put + CRC phase; put, crc32: the same work as two
                separate passes, timed outside the step
+  ceiling      a plain streaming kernel with the fetch's 1:2 byte mix, and the
+               fetch as a fraction of it
   cpu_baseline the CPU oracle on a bounded sample of the same workload
 
 Algorithmic bytes (what each step of the method covers):
@@ -264,6 +266,7 @@ def main():
               flush=True)
         return
 
+    ceiling = stream_ceiling(dev, hkv, fetch_launch_bytes, fetch_gbps)
     separate = separate_put_crc(dev, hkv, L, nb, tb, H, src_k, src_v, put_tab, records, crc,
                                 put_bytes, crc_bytes)
     frames = frames_leg(dev, hkv, W, w, L, src_k, src_v, put_tab)
@@ -325,6 +328,7 @@ def main():
             "tokens_per_s": round(tokens_per_s, 0),
             "ms_80_layers": round(float(np.mean(fetch_span_ms)), 4),
         },
+        "ceiling": ceiling,
         "fetch_per_token_delta": {
             "gbps": round(fetch_bytes / (tok_ms * 1e-3) / 1e9, 1),
             "ms_80_layers": round(tok_ms, 4),
@@ -348,6 +352,35 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
+
+
+def stream_ceiling(dev, hkv, fetch_launch_bytes, fetch_gbps, nbuf=16, reps=64):
+    """The fetch's byte mix with nothing else to do: hkv_stream_probe reads
+    one fetch layer's worth of bytes (136 MB) and writes twice that, with the
+    fetch's store pattern, rotating over 16 buffer pairs (more than the
+    256 MB Infinity Cache).  HIP events on the current stream."""
+    import torch
+    n_read = 1040 * 1024 * 128          # 136,314,880 B: the codes and scales of one layer
+    src = [torch.full((n_read,), 7, dtype=torch.uint8, device=dev) for _ in range(nbuf)]
+    dst = [torch.empty(2 * n_read, dtype=torch.uint8, device=dev) for _ in range(nbuf)]
+    s = torch.cuda.current_stream(dev)
+    for i in range(2 * nbuf):
+        hkv.stream_probe(src[i % nbuf], dst[i % nbuf], stream=s)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record(s)
+    for i in range(reps):
+        hkv.stream_probe(src[i % nbuf], dst[i % nbuf], stream=s)
+    ev[1].record(s)
+    s.synchronize()
+    ms = ev[0].elapsed_time(ev[1]) / reps
+    gbps = 3 * n_read / (ms * 1e-3) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"kernel": "hkv_stream_probe: 1 byte read for 2 written, 136 MB read per launch, "
+                      "the fetch's non-temporal store pattern",
+            "gbps": round(gbps, 1),
+            "us_per_launch": round(ms * 1e3, 2),
+            "fetch_frac_of_ceiling": round(fetch_gbps / gbps, 4)}
 
 
 def separate_put_crc(dev, hkv, L, nb, tb, H, src_k, src_v, put_tab, records, crc, put_bytes,

@@ -329,6 +329,14 @@ int hkv_select_top_tokens(const float* drift, int32_t n_tokens, int32_t k,
  * is negative or above 2^30. */
 int64_t hkv_select_workspace_bytes(int32_t n_tokens);
 
+/* Measurement aid, not a step of the method: a plain streaming kernel with
+ * the fetch's byte mix.  Reads bytes_read bytes of src and writes 2 *
+ * bytes_read bytes to dst (each 16 bytes twice, as two non-temporal 16-byte
+ * stores 128 bytes apart), so a benchmark can state the fetch as a fraction
+ * of what a kernel that only moves bytes in that ratio reaches.  bytes_read:
+ * a multiple of 128; src, dst: device, 16-byte aligned, not overlapping. */
+int hkv_stream_probe(const void* src, void* dst, int64_t bytes_read, hipStream_t stream);
+
 /* Host-only helpers. */
 
 /* Bytes of one record: 2*N*C + 4*N (see hkv_records); -1 on bad arguments. */

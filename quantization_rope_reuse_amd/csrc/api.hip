@@ -339,6 +339,13 @@ int hkv_token_drift(const void* h_cached, const void* h_fresh, int32_t n_tokens,
                                      row_stride * es, drift_out, stream));
 }
 
+int hkv_stream_probe(const void* src, void* dst, int64_t bytes_read, hipStream_t stream) {
+  if (bytes_read < 0 || bytes_read % 128 != 0) return HKV_ERR_INVALID_ARG;
+  if (bytes_read == 0) return HKV_OK;
+  if (!src || !dst || !aligned16(src) || !aligned16(dst)) return HKV_ERR_INVALID_ARG;
+  return to_status(hkv::launch_stream_expand(src, dst, bytes_read / 16, stream));
+}
+
 int64_t hkv_select_workspace_bytes(int32_t n_tokens) {
   if (n_tokens < 0 || n_tokens > kMaxSelectTokens) return -1;
   return hkv::select_workspace_bytes(n_tokens);

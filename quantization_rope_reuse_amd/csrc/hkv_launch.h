@@ -54,6 +54,9 @@ hipError_t launch_crc32_merge(const Geometry& g, int64_t record_bytes, const int
                               int32_t num_pages, const uint32_t* partials, uint32_t* out,
                               hipStream_t stream);
 
+// Measurement aid: read units16 x 16 bytes, write each twice (1:2 stream).
+hipError_t launch_stream_expand(const void* src, void* dst, int64_t units16, hipStream_t stream);
+
 // Frames: a kFrameHeaderBytes header, then the record.
 constexpr int64_t kFrameHeaderBytes = 64;
 

@@ -103,6 +103,8 @@ def lib():
         l.hkv_frame_verify.argtypes = [P(Shape), ctypes.c_int32, P(Records), ctypes.c_int32,
                                        vp, vp]
         l.hkv_frame_delta_m.argtypes = [P(Shape), ctypes.c_int32, P(Records), vp, vp, vp]
+        l.hkv_stream_probe.argtypes = [vp, vp, ctypes.c_int64, vp]
+        l.hkv_stream_probe.restype = ctypes.c_int
         l.hkv_stream_pair_create.argtypes = [ctypes.c_int32, P(vp), P(vp)]
         l.hkv_stream_pair_create.restype = ctypes.c_int
         l.hkv_stream_destroy.argtypes = [vp]
@@ -471,3 +473,16 @@ def frame_delta_m(frames, fmt, block_tokens: int, n_kv_heads: int, m_new, out=No
                                  _stream(stream, frames.device))
     _check("hkv_frame_delta_m", st)
     return out
+
+
+def stream_probe(src, dst, stream=None):
+    """Measurement aid: read src (uint8, a multiple of 128 bytes) and write it
+    twice into dst (twice the size) with the fetch's store pattern."""
+    if src.dtype != torch.uint8 or dst.dtype != torch.uint8:
+        raise ValueError("src and dst must be uint8 tensors")
+    if not src.is_contiguous() or not dst.is_contiguous() or dst.numel() < 2 * src.numel():
+        raise ValueError("dst must be contiguous and hold twice src")
+    _check("hkv_stream_probe", lib().hkv_stream_probe(
+        ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(dst.data_ptr()), src.numel(),
+        _stream(stream, src.device)))
+    return dst

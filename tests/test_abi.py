@@ -19,7 +19,7 @@ def test_exports_every_declared_symbol():
                           "hkv_select_top_tokens", "hkv_frame_headers", "hkv_frame_verify",
                           "hkv_frame_delta_m", "hkv_select_workspace_bytes",
                           "hkv_quant_fp8_crc", "hkv_quant_int4_crc",
-                          "hkv_quant_crc_workspace_bytes"}
+                          "hkv_quant_crc_workspace_bytes", "hkv_stream_probe"}
     lib = H.lib()
     for n in names:
         assert getattr(lib, n) is not None
@@ -325,3 +325,14 @@ def test_fused_put_crc_rejects_bad_arguments():
     assert call(wsb=need - 1) == H.ERR_INVALID_ARG
     assert call(ws=FAKE + 4100) == H.ERR_INVALID_ARG               # misaligned
     assert call(sh=_shape(n_blocks=0), crc=0, ws=0, wsb=0) == H.OK
+
+
+def test_stream_probe_rejects_bad_arguments():
+    lib = H.lib()
+    call = lambda src=FAKE, dst=FAKE + (1 << 20), n=1024: lib.hkv_stream_probe(
+        ctypes.c_void_p(src), ctypes.c_void_p(dst), n, None)
+    assert call(n=1000) == H.ERR_INVALID_ARG          # not a multiple of 128
+    assert call(n=-128) == H.ERR_INVALID_ARG
+    assert call(src=0) == H.ERR_INVALID_ARG
+    assert call(dst=FAKE + 8) == H.ERR_INVALID_ARG
+    assert call(n=0, src=0, dst=0) == H.OK

@@ -234,6 +234,22 @@ def test_fused_put_crc(fmt, shape):
             assert (got[:, b] == 0x1234567).all(), f"skipped block {b} CRC was written"
 
 
+def test_stream_probe_pattern():
+    """The measurement aid's output: every 16-byte unit i of the source lands
+    at output unit (i // 8) * 16 + i % 8 and, xor 0x5A5A5A5A, 8 units later."""
+    rng = np.random.default_rng(73)
+    src_np = rng.integers(0, 256, 128 * 37, dtype=np.uint8)
+    src = torch.from_numpy(src_np).to(DEV)
+    dst = torch.zeros(2 * src.numel(), dtype=torch.uint8, device=DEV)
+    hkv.stream_probe(src, dst)
+    torch.cuda.synchronize()
+    s16 = src_np.view(np.uint32).reshape(-1, 4)
+    d16 = dst.cpu().numpy().view(np.uint32).reshape(-1, 4)
+    i = np.arange(s16.shape[0])
+    o = (i // 8) * 16 + i % 8
+    assert np.array_equal(d16[o], s16) and np.array_equal(d16[o + 8], s16 ^ np.uint32(0x5A5A5A5A))
+
+
 def test_scale_edge_cases_fp32_source():
     """All-zero vectors (with signed zeros), scales that underflow or
     overflow fp16, and saturation beyond 448."""

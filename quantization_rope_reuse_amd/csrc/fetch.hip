@@ -136,19 +136,24 @@ __device__ __forceinline__ int pair_of(int sub, int j) {
     return 8 * sub + j;
 }
 
-// (cos, sin) of the 8 pairs this lane rotates for vector v, per-token delta.
-// Called by every lane of the wave (the shared-token path exchanges values
-// across lanes); the token index is clamped so that lanes past the end of
-// the chunk read a valid delta whose result they then discard.
-template <int PAIRS>
-__device__ __forceinline__ void token_angles(const FetchParams& p, int blk, int v, int lane,
-                                             int sub, float (&cs)[8], float (&sn)[8]) {
+// The per-token delta of vector v's token; the token index is clamped so
+// that lanes past the end of the chunk read a valid delta whose result they
+// then discard.
+__device__ __forceinline__ int token_delta(const FetchParams& p, int blk, int v) {
   const int t = min(v / p.n_heads, p.block_tokens - 1);
-  const int dm = p.delta[static_cast<int64_t>(blk) * p.block_tokens + t];
+  return p.delta[static_cast<int64_t>(blk) * p.block_tokens + t];
+}
+
+// (cos, sin) of the 8 pairs this lane rotates, for the delta dm of its
+// vector's token.  Called by every lane of the wave (the shared-token path
+// exchanges values across lanes).
+template <int PAIRS>
+__device__ __forceinline__ void token_angles(const FetchParams& p, int dm, double theta_lane,
+                                             int sub, float (&cs)[8], float (&sn)[8]) {
   if (p.n_heads % kVecsPerWave == 0) {
     // the pass's 8 vectors share one token: lane i computes pair i
     float cf, sf;
-    sincos_reduced(dm, p.theta[lane], &cf, &sf);
+    sincos_reduced(dm, theta_lane, &cf, &sf);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       cs[j] = __shfl(cf, pair_of<PAIRS>(sub, j));
@@ -200,16 +205,27 @@ __global__ __launch_bounds__(kThreads) void fetch_kernel(FetchParams p) {
   const int v0 = chunk * p.vecs_per_chunk + wave * kWaveVecs;
   if (v0 >= v_end) return;                      // whole wave idle
 
-  // Lane L holds the scale of vector v0 + (L mod kWaveVecs).
-  const int sv = v0 + (lane % kWaveVecs);
-  uint32_t my_scale = 0;
-  if (sv < v_end) my_scale = scales[sv];
+  // Loads complete in issue order, so everything the angle setup needs is
+  // loaded before the codes (unconditionally: a load under a divergent branch
+  // is waited for inside it), and the angles are computed while the codes are
+  // in flight: this lane's theta, and for per-token deltas its tokens' deltas.
+  const double theta_lane = p.theta[lane];
+  int tok_dm[kFetchPasses];
+  if constexpr (PER_TOKEN) {
+#pragma unroll
+    for (int i = 0; i < kFetchPasses; ++i)
+      tok_dm[i] = token_delta(p, blk, v0 + kVecsPerWave * i + vsub);
+  }
+
+  // Lane L holds the scale of vector v0 + (L mod kWaveVecs) (clamped to the
+  // chunk: lanes past its end load a valid scale they never use).
+  const uint32_t my_scale = scales[min(v0 + (lane % kWaveVecs), v_end - 1)];
+  // Unconditional as well (lanes past the chunk's end load its last vector
+  // and discard it): the loads before them can then be waited for alone.
   RawCodes<FMT> raw[kFetchPasses];
 #pragma unroll
-  for (int i = 0; i < kFetchPasses; ++i) {
-    const int v = v0 + kVecsPerWave * i + vsub;
-    if (v < v_end) raw[i] = load_codes<FMT>(codes, v, sub);
-  }
+  for (int i = 0; i < kFetchPasses; ++i)
+    raw[i] = load_codes<FMT>(codes, min(v0 + kVecsPerWave * i + vsub, v_end - 1), sub);
 
   if (page < 0 || page >= p.num_pages) return;   // skipped block: nothing stored
   char* out = (kv ? p.v_out : p.k_out) + layer * p.o_layer + page * p.o_page;
@@ -223,7 +239,7 @@ __global__ __launch_bounds__(kThreads) void fetch_kernel(FetchParams p) {
   float cs[8], sn[8];
   if (rotate) {
     double sd, cd;
-    sincos(static_cast<double>(dm) * p.theta[lane], &sd, &cd);
+    sincos(static_cast<double>(dm) * theta_lane, &sd, &cd);
     const float cf = static_cast<float>(cd);
     const float sf = static_cast<float>(sd);
 #pragma unroll
@@ -238,7 +254,7 @@ __global__ __launch_bounds__(kThreads) void fetch_kernel(FetchParams p) {
     const int v = v0 + kVecsPerWave * i + vsub;
     const float s = f16_bits_to_f32(__shfl(my_scale, kVecsPerWave * i + vsub));
     if constexpr (PER_TOKEN) {
-      if (kv == 0) token_angles<PAIRS>(p, blk, v, lane, sub, cs, sn);   // all lanes
+      if (kv == 0) token_angles<PAIRS>(p, tok_dm[i], theta_lane, sub, cs, sn);   // all lanes
     }
     if (v < v_end) {
       float a[8], b[8];

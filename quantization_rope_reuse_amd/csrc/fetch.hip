@@ -11,9 +11,10 @@
 // моделями и узлами"), module13.py listing, rope_cache / apply_rope.
 //
 // Work decomposition: one workgroup (4 waves) per (layer, block, K|V, chunk of
-// 64 vectors); each wave owns 16 consecutive vectors and moves them in 2
-// passes of 8 vectors, 8 lanes per vector.  Small workgroups measured best
-// on MI355X (about 16k workgroups per Llama-3-70B-shaped layer).  Every lane
+// vectors); each wave owns 8 consecutive vectors per pass, 8 lanes per
+// vector, and makes one pass (FP8 with per-block deltas: chunks of 32
+// vectors) or two (INT4, per-token deltas: chunks of 64).  Small workgroups
+// measured best on MI355X (about 33k workgroups per Llama-3-70B-shaped layer).  Every lane
 // of a key workgroup needs 8 (cos, sin) pairs; the 64 lanes of a wave first
 // compute one pair each (i = lane) in double precision and then gather the 8
 // they need with cross-lane reads, so the angle setup costs one double sincos
@@ -165,8 +166,8 @@ __device__ __forceinline__ void token_angles(const FetchParams& p, int dm, doubl
   }
 }
 
-// Each wave owns kFetchPasses * 8 consecutive vectors of its workgroup's
-// chunk and moves them in kFetchPasses passes of 8.  All loads of the wave
+// Each wave owns PASSES * 8 consecutive vectors of its workgroup's chunk and
+// moves them in PASSES passes of 8.  All loads of the wave
 // are issued before its first store: one counter tracks a wave's loads and
 // stores in issue order, so a load issued after a store could not be waited
 // for without also waiting for that store.  Stores are non-temporal: the
@@ -176,7 +177,7 @@ __device__ __forceinline__ void token_angles(const FetchParams& p, int dm, doubl
 // its own token's delta.  When the head count is a multiple of 8 the 8
 // vectors of a pass belong to one token and lane i computes pair i's angle
 // once per pass; otherwise each lane computes the 8 angles it needs.
-template <int FMT, int ODT, int PAIRS, bool PER_TOKEN>
+template <int FMT, int ODT, int PAIRS, bool PER_TOKEN, int PASSES>
 __global__ __launch_bounds__(kThreads) void fetch_kernel(FetchParams p) {
   const int layer = blockIdx.y;
   const int chunk = blockIdx.x % p.chunks;
@@ -200,7 +201,7 @@ __global__ __launch_bounds__(kThreads) void fetch_kernel(FetchParams p) {
   const int wave = threadIdx.x / kWave;
   const int sub = lane & (kLanesPerVec - 1);
   const int vsub = lane / kLanesPerVec;
-  constexpr int kWaveVecs = kVecsPerWave * kFetchPasses;
+  constexpr int kWaveVecs = kVecsPerWave * PASSES;
   const int v_end = min((chunk + 1) * p.vecs_per_chunk, p.vecs);
   const int v0 = chunk * p.vecs_per_chunk + wave * kWaveVecs;
   if (v0 >= v_end) return;                      // whole wave idle
@@ -210,10 +211,10 @@ __global__ __launch_bounds__(kThreads) void fetch_kernel(FetchParams p) {
   // is waited for inside it), and the angles are computed while the codes are
   // in flight: this lane's theta, and for per-token deltas its tokens' deltas.
   const double theta_lane = p.theta[lane];
-  int tok_dm[kFetchPasses];
+  int tok_dm[PASSES];
   if constexpr (PER_TOKEN) {
 #pragma unroll
-    for (int i = 0; i < kFetchPasses; ++i)
+    for (int i = 0; i < PASSES; ++i)
       tok_dm[i] = token_delta(p, blk, v0 + kVecsPerWave * i + vsub);
   }
 
@@ -222,9 +223,9 @@ __global__ __launch_bounds__(kThreads) void fetch_kernel(FetchParams p) {
   const uint32_t my_scale = scales[min(v0 + (lane % kWaveVecs), v_end - 1)];
   // Unconditional as well (lanes past the chunk's end load its last vector
   // and discard it): the loads before them can then be waited for alone.
-  RawCodes<FMT> raw[kFetchPasses];
+  RawCodes<FMT> raw[PASSES];
 #pragma unroll
-  for (int i = 0; i < kFetchPasses; ++i)
+  for (int i = 0; i < PASSES; ++i)
     raw[i] = load_codes<FMT>(codes, min(v0 + kVecsPerWave * i + vsub, v_end - 1), sub);
 
   if (page < 0 || page >= p.num_pages) return;   // skipped block: nothing stored
@@ -250,7 +251,7 @@ __global__ __launch_bounds__(kThreads) void fetch_kernel(FetchParams p) {
   }
 
 #pragma unroll
-  for (int i = 0; i < kFetchPasses; ++i) {
+  for (int i = 0; i < PASSES; ++i) {
     const int v = v0 + kVecsPerWave * i + vsub;
     const float s = f16_bits_to_f32(__shfl(my_scale, kVecsPerWave * i + vsub));
     if constexpr (PER_TOKEN) {
@@ -280,12 +281,30 @@ __global__ __launch_bounds__(kThreads) void fetch_kernel(FetchParams p) {
   }
 }
 
-template <int FMT, int ODT, int PAIRS, bool PT>
-hipError_t launch_t(const FetchParams& p, const Geometry& g, hipStream_t stream) {
+// Passes per wave, measured on MI355X: per-block-delta FP8 fetches are
+// fastest with one pass (8 vectors per wave, 32 per workgroup); INT4 records
+// (half the bytes per vector) and per-token deltas (more angle work per
+// vector) need the second pass's loads in flight to cover their latency.
+template <int FMT, bool PT>
+constexpr int fetch_passes() {
+  return (FMT == kFP8 && !PT) ? 1 : 2;
+}
+
+template <int FMT, int ODT, int PAIRS, bool PT, int PASSES>
+hipError_t launch_passes(FetchParams p, const Geometry& g, hipStream_t stream) {
+  // Workgroups of 4 waves x PASSES x 8 vectors.
+  p.vecs_per_chunk = kVecsPerWave * PASSES * (kThreads / kWave);
+  p.chunks = (g.vecs + p.vecs_per_chunk - 1) / p.vecs_per_chunk;
   dim3 grid(static_cast<unsigned>(g.n_blocks) * 2u * static_cast<unsigned>(p.chunks),
             static_cast<unsigned>(g.n_layers));
-  hipLaunchKernelGGL((fetch_kernel<FMT, ODT, PAIRS, PT>), grid, dim3(kThreads), 0, stream, p);
+  hipLaunchKernelGGL((fetch_kernel<FMT, ODT, PAIRS, PT, PASSES>), grid, dim3(kThreads), 0, stream,
+                     p);
   return hipGetLastError();
+}
+
+template <int FMT, int ODT, int PAIRS, bool PT>
+hipError_t launch_t(const FetchParams& p, const Geometry& g, hipStream_t stream) {
+  return launch_passes<FMT, ODT, PAIRS, PT, fetch_passes<FMT, PT>()>(p, g, stream);
 }
 
 template <int FMT, int ODT, bool PT>
@@ -335,9 +354,6 @@ hipError_t launch_fetch(int fmt, int dst_dtype, int pairs, const Geometry& g,
   p.num_pages = dst.num_pages;
   p.n_heads = g.n_heads;
   p.vecs = g.vecs;
-  // Workgroups of kFetchGroupVecs vectors (4 waves x kFetchPasses passes).
-  p.chunks = (g.vecs + kFetchGroupVecs - 1) / kFetchGroupVecs;
-  p.vecs_per_chunk = kFetchGroupVecs;
   for (int i = 0; i < kHeadDim / 2; ++i)
     p.theta[i] = 1.0 / pow(rope_base, static_cast<double>(2 * i) / kHeadDim);
   return delta_per_token ? launch_fmt<true>(fmt, dst_dtype, pairs, p, g, stream)

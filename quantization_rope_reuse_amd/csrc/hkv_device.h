@@ -20,8 +20,7 @@ constexpr int kWave = 64;
 constexpr int kThreads = 256;                          // 4 waves per workgroup
 constexpr int kVecsPerWave = kWave / kLanesPerVec;     // 8
 constexpr int kVecsPerPass = kThreads / kLanesPerVec;  // 32
-constexpr int kFetchPasses = 2;                        // fetch: passes per wave
-constexpr int kFetchGroupVecs = kVecsPerWave * kFetchPasses * (kThreads / kWave);   // 64
+constexpr int kFetchMinGroupVecs = kVecsPerWave * (kThreads / kWave);  // 32: smallest fetch chunk
 constexpr int kQuantPasses = 2;                        // put: passes per wave
 constexpr int kQuantGroupVecs = kVecsPerWave * kQuantPasses * (kThreads / kWave);   // 64
 

@@ -163,8 +163,8 @@ int quant_crc_common(int32_t fmt, const hkv_shape* shape, const hkv_pages* src,
   const hipError_t e = hkv::launch_quant_crc_units(fmt, src_dtype, g, pv, block_table, rv, rb,
                                                    partials, stream);
   if (e != hipSuccess) return HKV_ERR_HIP;
-  return to_status(hkv::launch_crc32_merge(g, rb, block_table, pv.num_pages, partials, crc_out,
-                                           stream));
+  return to_status(hkv::launch_crc32_merge(g, rb, rv, block_table, pv.num_pages, partials,
+                                           crc_out, stream));
 }
 
 int fetch_common(const hkv_shape* shape, int32_t fmt, const hkv_records* src,

@@ -138,42 +138,69 @@ __global__ __launch_bounds__(kThreads) void crc32_kernel(CrcParams p) {
 }
 
 // Merge of the fused put + CRC: `partials` holds, for every record, the raw
-// CRC of each of its `units` 128-byte units (record bytes / 128, written by
-// the put).  Lane i takes units i, i+64, i+128, ... (leading zero units pad
-// the count to a multiple of 64) and advances c <- c * x^(8*128*64) xor
-// raw(unit), the constant multiplication being four lookups in a table built
-// per workgroup; the 64 lane values merge with shifts x^(8 * 128 * 2^k).
-// Records of skipped blocks (table entry negative or >= num_pages) are left
-// alone.
+// CRC of each 128-byte unit of its codes (the first code_units of its
+// `units` units, written by the put).  The remaining units hold the record's
+// scales; the merge feeds those itself from the record (the lanes that meet
+// one feed its 32 words through the byte tables T, read back from HBM).
+// Lane i takes units i, i+64, i+128, ... (leading zero units pad the count
+// to a multiple of 64) and advances c <- c * x^(8*128*64) xor raw(unit),
+// the constant multiplication being four lookups in the tables M, built per
+// workgroup from 32 basis values computed on the host; the 64 lane values
+// merge with shifts x^(8 * 128 * 2^k).  Records of skipped blocks (table
+// entry negative or >= num_pages) are left alone.
 struct MergeParams {
   const uint32_t* partials;
+  const uint8_t* rec;
+  int64_t rec_layer, rec_block;
   const int32_t* table;
   uint32_t* out;
   int32_t n_blocks, n_records, num_pages;
-  int32_t units, pad, per_lane;
-  uint32_t mul_lanes;        // x^(8 * 128 * 64) mod P
+  int32_t units, code_units, pad, per_lane;
+  uint32_t m_basis[4][8];    // (1 << (8k + i)) * x^(8 * 128 * 64) mod P
   uint32_t shift[6];         // x^(8 * 128 * 2^k) mod P
   uint32_t init_term;        // 0xFFFFFFFF * x^(8 * record bytes) mod P
 };
 
 __global__ __launch_bounds__(kThreads) void crc32_merge_kernel(MergeParams p) {
-  __shared__ uint32_t M[4][256];                 // M[k][b] = (b at byte k) * mul_lanes
+  __shared__ uint32_t M[4][256];                 // M[k][b] = (b at byte k) * x^(8*128*64)
+  __shared__ uint32_t T[4][256];
   const int tid = threadIdx.x;
 #pragma unroll
-  for (int k = 0; k < 4; ++k)
-    M[k][tid] = crc_mulmod(static_cast<uint32_t>(tid) << (8 * k), p.mul_lanes);
-  __syncthreads();
+  for (int k = 0; k < 4; ++k) {
+    uint32_t m = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) m ^= p.m_basis[k][i] & (0u - ((static_cast<uint32_t>(tid) >> i) & 1u));
+    M[k][tid] = m;
+  }
+  build_crc_tables(T);                           // ends with a barrier
   const int lane = tid & (kWave - 1);
   const int r = blockIdx.x * kRecordsPerGroup + tid / kWave;
-  if (r >= p.n_records) return;                 // whole wave, after the barrier
-  const int blk = r % p.n_blocks;
+  if (r >= p.n_records) return;                 // whole wave, after the barriers
+  const int layer = r / p.n_blocks;
+  const int blk = r - layer * p.n_blocks;
   const int page = p.table[blk];
   if (page < 0 || page >= p.num_pages) return;
   const uint32_t* part = p.partials + static_cast<int64_t>(r) * p.units;
+  const uint8_t* rec = p.rec + layer * p.rec_layer + blk * p.rec_block;
   uint32_t c = 0;
   for (int j = 0; j < p.per_lane; ++j) {
     const int u = lane + kWave * j - p.pad;
-    const uint32_t w = u >= 0 ? part[u] : 0u;
+    uint32_t w = 0;
+    if (u >= p.code_units) {                     // a scale unit: feed it here
+      const u32x4* src = reinterpret_cast<const u32x4*>(rec + static_cast<int64_t>(u) * 128);
+      u32x4 x[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) x[q] = src[q];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        w = crc_feed_word(T, w, x[q][0]);
+        w = crc_feed_word(T, w, x[q][1]);
+        w = crc_feed_word(T, w, x[q][2]);
+        w = crc_feed_word(T, w, x[q][3]);
+      }
+    } else if (u >= 0) {
+      w = part[u];
+    }
     c = M[0][c & 0xFFu] ^ M[1][(c >> 8) & 0xFFu] ^ M[2][(c >> 16) & 0xFFu] ^ M[3][c >> 24] ^ w;
   }
 #pragma unroll
@@ -216,11 +243,14 @@ hipError_t launch_crc32(const Geometry& g, int64_t record_bytes, const RecordVie
   return hipGetLastError();
 }
 
-hipError_t launch_crc32_merge(const Geometry& g, int64_t record_bytes, const int32_t* table,
-                              int32_t num_pages, const uint32_t* partials, uint32_t* out,
-                              hipStream_t stream) {
+hipError_t launch_crc32_merge(const Geometry& g, int64_t record_bytes, const RecordView& src,
+                              const int32_t* table, int32_t num_pages, const uint32_t* partials,
+                              uint32_t* out, hipStream_t stream) {
   MergeParams p;
   p.partials = partials;
+  p.rec = src.base;
+  p.rec_layer = src.layer;
+  p.rec_block = src.block;
   p.table = table;
   p.out = out;
   p.n_blocks = g.n_blocks;
@@ -230,7 +260,11 @@ hipError_t launch_crc32_merge(const Geometry& g, int64_t record_bytes, const int
   p.units = static_cast<int32_t>(units);
   p.pad = static_cast<int32_t>((kWave - units % kWave) % kWave);
   p.per_lane = static_cast<int32_t>((units + p.pad) / kWave);
-  p.mul_lanes = crc_x8n(static_cast<uint64_t>(128) * kWave);
+  // the scales (2 x vecs fp16) close the record; everything before is codes
+  p.code_units = static_cast<int32_t>((record_bytes - 4LL * g.vecs) / 128);
+  const uint32_t mul_lanes = crc_x8n(static_cast<uint64_t>(128) * kWave);
+  for (int k = 0; k < 4; ++k)
+    for (int i = 0; i < 8; ++i) p.m_basis[k][i] = crc_mulmod(1u << (8 * k + i), mul_lanes);
   for (int k = 0; k < 6; ++k) p.shift[k] = crc_x8n(static_cast<uint64_t>(128) << k);
   p.init_term = crc_mulmod(0xFFFFFFFFu, crc_x8n(static_cast<uint64_t>(record_bytes)));
   const unsigned groups =

@@ -44,15 +44,17 @@ hipError_t launch_crc32(const Geometry& g, int64_t record_bytes, const RecordVie
                         uint32_t* out, hipStream_t stream);
 
 // Fused put + CRC: the put also writes the raw CRC of every 128-byte unit of
-// every record to `partials` (layer-major, record_bytes / 128 per record);
-// requires g.vecs % 64 == 0.  The merge turns them into the records' CRCs.
+// the codes of every record to `partials` (layer-major, record_bytes / 128
+// slots per record, the scale units' slots unused); requires
+// g.vecs % 64 == 0.  The merge reads the scale units back from the records
+// and turns both into the records' CRCs.
 hipError_t launch_quant_crc_units(int fmt, int src_dtype, const Geometry& g, const PageView& src,
                                   const int32_t* table, const RecordView& dst,
                                   int64_t record_bytes, uint32_t* partials, hipStream_t stream);
 
-hipError_t launch_crc32_merge(const Geometry& g, int64_t record_bytes, const int32_t* table,
-                              int32_t num_pages, const uint32_t* partials, uint32_t* out,
-                              hipStream_t stream);
+hipError_t launch_crc32_merge(const Geometry& g, int64_t record_bytes, const RecordView& src,
+                              const int32_t* table, int32_t num_pages, const uint32_t* partials,
+                              uint32_t* out, hipStream_t stream);
 
 // Measurement aid: read units16 x 16 bytes, write each twice (1:2 stream).
 hipError_t launch_stream_expand(const void* src, void* dst, int64_t units16, hipStream_t stream);

@@ -174,11 +174,14 @@ __device__ __forceinline__ uint32_t quant_vector(float (&a)[8], float (&b)[8], u
 //
 // CRC (fused put + CRC-32, chunks of exactly kQuantGroupVecs vectors): the
 // workgroup's codes form a contiguous run of the record (8 KB FP8, 4 KB
-// INT4) and its 64 scales another one (128 B); both are staged in LDS as they
-// are written, and after a barrier one thread per 128-byte unit feeds its
-// unit into a zero CRC register (byte tables in LDS) and stores that raw
-// value in `partials` at the unit's index in the record.  A second kernel
-// merges the units of each record (crc.hip).
+// INT4), staged in LDS as they are written; after a barrier one thread per
+// 128-byte unit (64 FP8 units: exactly the first wave) feeds its unit into a
+// zero CRC register (byte tables in LDS) and stores that raw value in
+// `partials` at the unit's index in the record.  The byte tables are built
+// while the source loads are in flight.  The scale units at the end of the
+// record are left to the merge kernel (crc.hip), which reads them back: a
+// 65th thread here would run a whole second wave's chain for one unit, and
+// measured 8% slower.
 template <int FMT, int SDT, bool CRC>
 __global__ __launch_bounds__(kThreads) void quant_kernel(QuantParams p) {
   const int layer = blockIdx.y;
@@ -191,9 +194,7 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(QuantParams p) {
 
   constexpr int kCB = FMT == kFP8 ? kHeadDim : kHeadDim / 2;
   __shared__ __align__(16) uint8_t stage[CRC ? kQuantGroupVecs * kCB : 16];
-  __shared__ __align__(16) uint16_t stage_scales[CRC ? kQuantGroupVecs : 8];
   __shared__ uint32_t T[CRC ? 4 : 1][256];
-  if constexpr (CRC) build_crc_tables(T);
 
   constexpr int CB = FMT == kFP8 ? kHeadDim : kHeadDim / 2;
   constexpr int ES = ElemSize<SDT>::value;
@@ -228,6 +229,9 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(QuantParams p) {
         rb[i] = load_run<SDT>(x_ptr + 64 * ES);
       }
     }
+    if constexpr (CRC) {
+      if (i0 == 0) build_crc_tables(T);        // every thread; ends with a barrier
+    }
 #pragma unroll
     for (int i = 0; i < kBatch; ++i) {
       const int v = v0 + kVecsPerWave * (i0 + i) + vsub;
@@ -247,17 +251,13 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(QuantParams p) {
       if (lane / kLanesPerVec == i0 + i) my_scale = got;
     }
   }
-  if (lane < kWaveVecs && v0 + lane < v_end) {
-    scales[v0 + lane] = static_cast<uint16_t>(my_scale);
-    if constexpr (CRC) stage_scales[v0 - chunk_v0 + lane] = static_cast<uint16_t>(my_scale);
-  }
+  if (lane < kWaveVecs && v0 + lane < v_end) scales[v0 + lane] = static_cast<uint16_t>(my_scale);
   if constexpr (CRC) {
     __syncthreads();
     constexpr int kCodeUnits = kQuantGroupVecs * CB / 128;
     const int u = threadIdx.x;
-    if (u <= kCodeUnits) {                          // kCodeUnits: the scale unit
-      const u32x4* w = u < kCodeUnits ? reinterpret_cast<const u32x4*>(stage + u * 128)
-                                      : reinterpret_cast<const u32x4*>(stage_scales);
+    if (u < kCodeUnits) {
+      const u32x4* w = reinterpret_cast<const u32x4*>(stage + u * 128);
       uint32_t c = 0;
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
@@ -267,9 +267,8 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(QuantParams p) {
         c = crc_feed_word(T, c, x[2]);
         c = crc_feed_word(T, c, x[3]);
       }
-      const int64_t byte = u < kCodeUnits
-          ? static_cast<int64_t>(kv) * p.vecs * CB + static_cast<int64_t>(chunk_v0) * CB + u * 128
-          : 2LL * p.vecs * CB + 2LL * kv * p.vecs + 2LL * chunk_v0;
+      const int64_t byte =
+          static_cast<int64_t>(kv) * p.vecs * CB + static_cast<int64_t>(chunk_v0) * CB + u * 128;
       p.partials[(static_cast<int64_t>(layer) * (p.table_blocks) + blk) * p.units + byte / 128] = c;
     }
   }

@@ -222,7 +222,11 @@ def test_fused_put_crc(fmt, shape):
     rec2 = hkv.alloc_records(L, len(table), fmt, tb, H, device=DEV)
     rec2.fill_(0xA5)
     crc = torch.full((L, len(table)), 0x1234567, dtype=torch.int32, device=DEV)
-    hkv.quant_crc(fmt, kt, vt, _dev_i32(table), rec2, crc_out=crc)
+    # a workspace full of ones: a slot the merge reads without the put having
+    # written it would show in the CRCs
+    need = hkv.quant_crc_workspace_bytes(fmt, L, len(table), tb, H)
+    ws = torch.full((max(need, 16),), 0xFF, dtype=torch.uint8, device=DEV)
+    hkv.quant_crc(fmt, kt, vt, _dev_i32(table), rec2, crc_out=crc, workspace=ws)
     torch.cuda.synchronize()
     assert torch.equal(rec2, rec), "fused put wrote different records"
     got = crc_u32(crc)

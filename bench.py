@@ -272,6 +272,7 @@ def main():
     frames = frames_leg(dev, hkv, W, w, L, src_k, src_v, put_tab)
     select = recompute_select(dev, hkv, W)
     others = other_workloads(dev, hkv, W)
+    shard = tp8_shard(dev, hkv, W)
 
     if a.calibrate_copy:
         # torch.neg over 2**28 fp32 values: reads exactly 1 GiB, writes 1 GiB
@@ -347,6 +348,7 @@ def main():
         "put": separate["put"],
         "crc32": separate["crc32"],
         "other_workloads": others,
+        "tp8_shard": shard,
         "frames": frames,
         "recompute_select": select,
         "cpu_baseline": cpu,
@@ -471,6 +473,110 @@ def other_workloads(dev, hkv, W, reps=5):
         }
         del src_k, src_v, rec, out_k, out_v
         torch.cuda.empty_cache()
+    return res
+
+
+def tp8_shard(dev, hkv, W, reps=5):
+    """One GPU's share of the Llama-3-70B-shaped cache under tensor
+    parallelism over its 8 KV heads: one head, 131,072 vectors per layer
+    (17.0 MB read and 33.6 MB written per layer fetch).  Put and CRC in one
+    pass, then the 80 per-layer fetches on one stream, launched eagerly and
+    replayed from a HIP graph.  Outside the step; HIP events."""
+    import numpy as np
+    import torch
+    w = W.LLAMA3_70B_TP8
+    L, nb, tb, H = w.n_layers, w.n_blocks, w.block_tokens, w.n_kv_heads
+    src_k = torch.empty((L, nb, tb, H, 128), dtype=torch.bfloat16, device=dev)
+    src_v = torch.empty_like(src_k)
+    put_tab = torch.from_numpy(W.put_table(w)).to(dev)
+    tmp = torch.empty((w.n_tokens, H, 128), dtype=torch.float32, device=dev)
+    gen = torch.Generator(device=dev)
+    for l in range(L):
+        for kv, dst in ((0, src_k), (1, src_v)):
+            W.device_layer_values(w, l, kv, tmp, generator=gen)
+            dst[l].index_copy_(0, put_tab.long(), tmp.view(nb, tb, H, 128).to(torch.bfloat16))
+    del tmp
+    rec = hkv.alloc_records(L, nb, "fp8", tb, H, device=dev)
+    crc = torch.empty((L, nb), dtype=torch.int32, device=dev)
+    ws = torch.empty(hkv.quant_crc_workspace_bytes("fp8", L, nb, tb, H), dtype=torch.uint8,
+                     device=dev)
+    ftab = torch.from_numpy(W.fetch_table(w)).to(dev)
+    dm = torch.from_numpy(W.delta_m(w)).to(dev)
+    order = hkv.page_visit_order(ftab, nb)
+    out_k = torch.empty_like(src_k)
+    out_v = torch.empty_like(src_k)
+    rec_l = [rec[l:l + 1] for l in range(L)]
+    ok_l = [out_k[l:l + 1] for l in range(L)]
+    ov_l = [out_v[l:l + 1] for l in range(L)]
+    s = torch.cuda.current_stream(dev)
+
+    def fetch_all():
+        for l in range(L):
+            hkv.fetch_dequant_rope_shift(rec_l[l], "fp8", ftab, dm, w.rope_base, w.pairs,
+                                         ok_l[l], ov_l[l], visit_order=order, stream=s)
+
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    put_ms, fetch_ms = [], []
+    for rep in range(reps + 1):
+        ev[0].record(s)
+        hkv.quant_crc("fp8", src_k, src_v, put_tab, rec, crc_out=crc, workspace=ws, stream=s)
+        ev[1].record(s)
+        fetch_all()
+        ev[2].record(s)
+        s.synchronize()
+        if rep:
+            put_ms.append(ev[0].elapsed_time(ev[1]))
+            fetch_ms.append(ev[1].elapsed_time(ev[2]))
+    graph = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        for l in range(L):
+            hkv.fetch_dequant_rope_shift(rec_l[l], "fp8", ftab, dm, w.rope_base, w.pairs,
+                                         ok_l[l], ov_l[l], visit_order=order)
+    torch.cuda.synchronize()
+    cur = torch.cuda.current_stream(dev)
+    graph_ms = []
+    for rep in range(reps + 1):
+        ev[0].record(cur)
+        graph.replay()
+        ev[1].record(cur)
+        cur.synchronize()
+        if rep:
+            graph_ms.append(ev[0].elapsed_time(ev[1]))
+    del graph
+    # the same 80 layers in one call (one launch): the kernel without the
+    # per-launch ramp and drain
+    one_ms = []
+    for rep in range(reps + 1):
+        ev[0].record(s)
+        hkv.fetch_dequant_rope_shift(rec, "fp8", ftab, dm, w.rope_base, w.pairs, out_k, out_v,
+                                     visit_order=order, stream=s)
+        ev[1].record(s)
+        s.synchronize()
+        if rep:
+            one_ms.append(ev[0].elapsed_time(ev[1]))
+    vecs_layer = 2 * w.n_tokens * H
+    launch_bytes = vecs_layer * (130 + 256) + nb * 8
+    put_bytes = L * (vecs_layer * (256 + 130) + nb * 4)
+    crc_bytes = L * nb * (hkv.record_bytes("fp8", tb, H) + 4)
+    fms, gms, pms, oms = (float(np.mean(x)) for x in (fetch_ms, graph_ms, put_ms, one_ms))
+    res = {
+        "workload": "Llama-3-70B-shaped cache, one KV head (one GPU of TP = 8): 80 layers x "
+                    "65536 tokens x 1 head x d128 bf16, blocks of 64, dm=+8192",
+        "fetch_bytes_per_layer": launch_bytes,
+        "fetch_ms_80_layers": round(fms, 4),
+        "fetch_us_per_layer": round(fms * 1e3 / L, 2),
+        "fetch_gbps": round(L * launch_bytes / (fms * 1e-3) / 1e9, 1),
+        "fetch_frac_of_peak": round(L * launch_bytes / (fms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        "fetch_graph_ms_80_layers": round(gms, 4),
+        "fetch_graph_gbps": round(L * launch_bytes / (gms * 1e-3) / 1e9, 1),
+        "fetch_one_launch_ms_80_layers": round(oms, 4),
+        "fetch_one_launch_gbps": round(L * launch_bytes / (oms * 1e-3) / 1e9, 1),
+        "put_crc_ms": round(pms, 4),
+        "put_crc_gbps": round((put_bytes + crc_bytes) / (pms * 1e-3) / 1e9, 1),
+    }
+    del src_k, src_v, rec, out_k, out_v, rec_l, ok_l, ov_l
+    torch.cuda.empty_cache()
     return res
 
 

@@ -86,6 +86,14 @@ LLAMA3_70B = KVWorkload(
     rope_base=500000.0, pairs="half_split", formats=("fp8",),
     delta_kind="const", delta_value=8192)
 
+# One GPU's share of the Llama-3-70B-shaped cache under tensor parallelism
+# over its 8 KV heads (TP = 8): one head per GPU, everything else the same.
+LLAMA3_70B_TP8 = KVWorkload(
+    name="llama3_70b_tp8_shard_80L_1H_65536tok_bf16", n_layers=80, n_kv_heads=1,
+    n_tokens=65536, block_tokens=64, src_dtype="bf16", out_dtype="bf16",
+    rope_base=500000.0, pairs="half_split", formats=("fp8",),
+    delta_kind="const", delta_value=8192)
+
 INT4_L3 = KVWorkload(
     name="int4_l3_32L_8H_16384tok_fp16_outliers", n_layers=32, n_kv_heads=8,
     n_tokens=16384, block_tokens=64, src_dtype="f16", out_dtype="f16",
@@ -93,7 +101,7 @@ INT4_L3 = KVWorkload(
     delta_kind="uniform", delta_value=4096, outlier_frac=0.01,
     outlier_gain=20.0)
 
-ALL = (TINY, GQA_REORDER, QWEN3_8B, LLAMA3_70B, INT4_L3)
+ALL = (TINY, GQA_REORDER, QWEN3_8B, LLAMA3_70B, LLAMA3_70B_TP8, INT4_L3)
 
 # GQA reorder chunks (tokens): cached order [Sys, DocA, DocB, Q], reused as
 # [Sys, DocB, DocA, Q] (the HyperCache post's Part A experiment order).

@@ -162,6 +162,40 @@ def test_llama3_70b_full_layerwise_side_stream():
     _properties(src_k, src_v, put_tab, out_k, out_v, ftab, rel_v=0.08, rel_norm=0.08)
 
 
+def test_llama3_70b_tp8_shard():
+    """One GPU's tensor-parallel share of the Llama-3-70B-shaped cache: one KV
+    head, 64 vectors per block (two 32-vector fetch chunks, one fused put
+    chunk).  Put and CRC in one pass, 80 per-layer fetches on a side stream,
+    the same checks as the full cache."""
+    w = W.LLAMA3_70B_TP8
+    print(f"[full] {w.name}", flush=True)
+    src_k, src_v, put_tab = _fill_source(w)
+    L, nb = w.n_layers, w.n_blocks
+    rec = hkv.alloc_records(L, nb, "fp8", w.block_tokens, w.n_kv_heads, device=DEV)
+    crc = hkv.quant_crc("fp8", src_k, src_v, put_tab, rec)
+    ftab = torch.from_numpy(W.fetch_table(w)).to(DEV)
+    dm_np = W.delta_m(w)
+    dm = torch.from_numpy(dm_np).to(DEV)
+    out_k = canary_fill(torch.empty_like(src_k))
+    out_v = canary_fill(torch.empty_like(src_v))
+    side = torch.cuda.Stream()
+    ready = torch.cuda.Event()
+    ready.record(torch.cuda.current_stream())
+    side.wait_event(ready)
+    order = hkv.page_visit_order(ftab, nb, stream=side)
+    for l in range(L):
+        hkv.fetch_dequant_rope_shift(rec[l:l + 1], "fp8", ftab, dm, w.rope_base, w.pairs,
+                                     out_k[l:l + 1], out_v[l:l + 1], visit_order=order,
+                                     stream=side)
+    side.synchronize()
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(84)
+    for l, b in _samples(w, L, rng, 8):
+        _check_block(w, "fp8", l, b, src_k, src_v, put_tab.cpu().numpy(), rec, crc, out_k,
+                     out_v, ftab.cpu().numpy(), dm_np)
+    _properties(src_k, src_v, put_tab, out_k, out_v, ftab, rel_v=0.08, rel_norm=0.08)
+
+
 def test_int4_l3_full_with_tamper():
     w = W.INT4_L3
     print(f"[full] {w.name}", flush=True)

@@ -137,17 +137,20 @@ __global__ __launch_bounds__(kThreads) void crc32_kernel(CrcParams p) {
   if (lane == 0) p.out[r] = ~(p.init_term ^ crc);
 }
 
-// Merge of the fused put + CRC: `partials` holds, for every record, the raw
-// CRC of each 128-byte unit of its codes (the first code_units of its
-// `units` units, written by the put).  The remaining units hold the record's
-// scales; the merge feeds those itself from the record (the lanes that meet
-// one feed its 32 words through the byte tables T, read back from HBM).
-// Lane i takes units i, i+64, i+128, ... (leading zero units pad the count
-// to a multiple of 64) and advances c <- c * x^(8*128*64) xor raw(unit),
-// the constant multiplication being four lookups in the tables M, built per
-// workgroup from 32 basis values computed on the host; the 64 lane values
-// merge with shifts x^(8 * 128 * 2^k).  Records of skipped blocks (table
-// entry negative or >= num_pages) are left alone.
+// Merge of the fused put + CRC.  A record is [codes][scales]: code_units
+// 128-byte units of codes (a multiple of 64) whose raw CRCs the put wrote to
+// `partials`, then scale_bytes of fp16 scales (a multiple of 256), which the
+// merge reads back from the record.  One wave per record.  Lane i runs a
+// Horner chain over its code units i, i+64, i+128, ...:
+//   c <- c * x^(8*128*64) xor raw(unit)
+// (the constant multiplication is four lookups in the tables M), and feeds
+// its own scale_bytes/64 consecutive scale bytes into a zero register s
+// (byte tables T).  Unit i + 64j sits 64(n-1-j) + (63-i) units before the
+// end of the codes, so the record's raw CRC is the xor over the lanes of
+//   c * x^(8*128*(63-i) + 8*scale_bytes)  xor  s * x^(8*(scale_bytes/64)*(63-i)),
+// two GF(2) multiplications per lane by constants computed on the host, then
+// a butterfly xor over the wave.  Records of skipped blocks (table entry
+// negative or >= num_pages) are left alone.
 struct MergeParams {
   const uint32_t* partials;
   const uint8_t* rec;
@@ -155,10 +158,13 @@ struct MergeParams {
   const int32_t* table;
   uint32_t* out;
   int32_t n_blocks, n_records, num_pages;
-  int32_t units, code_units, pad, per_lane;
-  uint32_t m_basis[4][8];    // (1 << (8k + i)) * x^(8 * 128 * 64) mod P
-  uint32_t shift[6];         // x^(8 * 128 * 2^k) mod P
-  uint32_t init_term;        // 0xFFFFFFFF * x^(8 * record bytes) mod P
+  int32_t units;               // partial slots per record (record bytes / 128)
+  int32_t code_units;          // multiple of 64
+  int32_t scale_bytes;         // multiple of 256
+  uint32_t m_basis[4][8];      // (1 << (8k + i)) * x^(8 * 128 * 64) mod P
+  uint32_t code_shift[kWave];  // x^(8*128*(63-i) + 8*scale_bytes) mod P
+  uint32_t scale_shift[kWave]; // x^(8*(scale_bytes/64)*(63-i)) mod P
+  uint32_t init_term;          // 0xFFFFFFFF * x^(8 * record bytes) mod P
 };
 
 __global__ __launch_bounds__(kThreads) void crc32_merge_kernel(MergeParams p) {
@@ -180,38 +186,36 @@ __global__ __launch_bounds__(kThreads) void crc32_merge_kernel(MergeParams p) {
   const int blk = r - layer * p.n_blocks;
   const int page = p.table[blk];
   if (page < 0 || page >= p.num_pages) return;
-  const uint32_t* part = p.partials + static_cast<int64_t>(r) * p.units;
-  const uint8_t* rec = p.rec + layer * p.rec_layer + blk * p.rec_block;
-  uint32_t c = 0;
-  for (int j = 0; j < p.per_lane; ++j) {
-    const int u = lane + kWave * j - p.pad;
-    uint32_t w = 0;
-    if (u >= p.code_units) {                     // a scale unit: feed it here
-      const u32x4* src = reinterpret_cast<const u32x4*>(rec + static_cast<int64_t>(u) * 128);
-      u32x4 x[8];
+  const uint32_t* part = p.partials + static_cast<int64_t>(r) * p.units + lane;
+  const int per_lane = p.scale_bytes / kWave;    // bytes, a multiple of 4
+  const uint32_t* sc = reinterpret_cast<const uint32_t*>(
+      p.rec + layer * p.rec_layer + blk * p.rec_block + static_cast<int64_t>(p.code_units) * 128 +
+      static_cast<int64_t>(lane) * per_lane);
+  const uint32_t code_k = p.code_shift[lane];
+  const uint32_t scale_k = p.scale_shift[lane];
+  const int n = p.code_units / kWave;            // code units per lane
+  const int words = per_lane / 4;                 // scale words per lane
+  // Batches of 8 of each: a batch's 16 loads are issued before either chain
+  // consumes them (the batch guards are uniform over the wave).
+  uint32_t c = 0, sreg = 0;
+  for (int j0 = 0; j0 < n || j0 < words; j0 += 8) {
+    uint32_t w[8], x[8];
 #pragma unroll
-      for (int q = 0; q < 8; ++q) x[q] = src[q];
+    for (int i = 0; i < 8; ++i) w[i] = j0 + i < n ? part[static_cast<int64_t>(kWave) * (j0 + i)] : 0u;
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        w = crc_feed_word(T, w, x[q][0]);
-        w = crc_feed_word(T, w, x[q][1]);
-        w = crc_feed_word(T, w, x[q][2]);
-        w = crc_feed_word(T, w, x[q][3]);
-      }
-    } else if (u >= 0) {
-      w = part[u];
+    for (int i = 0; i < 8; ++i) x[i] = j0 + i < words ? sc[j0 + i] : 0u;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (j0 + i < n)
+        c = M[0][c & 0xFFu] ^ M[1][(c >> 8) & 0xFFu] ^ M[2][(c >> 16) & 0xFFu] ^ M[3][c >> 24] ^
+            w[i];
+      if (j0 + i < words) sreg = crc_feed_word(T, sreg, x[i]);
     }
-    c = M[0][c & 0xFFu] ^ M[1][(c >> 8) & 0xFFu] ^ M[2][(c >> 16) & 0xFFu] ^ M[3][c >> 24] ^ w;
   }
+  uint32_t v = crc_mulmod(c, code_k) ^ crc_mulmod(sreg, scale_k);
 #pragma unroll
-  for (int k = 0; k < 6; ++k) {
-    const uint32_t other = __shfl_xor(c, 1 << k);
-    const bool left = ((lane >> k) & 1) == 0;
-    const uint32_t lo = left ? c : other;       // earlier bytes
-    const uint32_t hi = left ? other : c;
-    c = crc_mulmod(lo, p.shift[k]) ^ hi;
-  }
-  if (lane == 0) p.out[r] = ~(p.init_term ^ c);
+  for (int k = 0; k < 6; ++k) v ^= __shfl_xor(v, 1 << k);
+  if (lane == 0) p.out[r] = ~(p.init_term ^ v);
 }
 
 }  // namespace
@@ -256,16 +260,22 @@ hipError_t launch_crc32_merge(const Geometry& g, int64_t record_bytes, const Rec
   p.n_blocks = g.n_blocks;
   p.n_records = g.n_layers * g.n_blocks;
   p.num_pages = num_pages;
-  const int64_t units = record_bytes / 128;
-  p.units = static_cast<int32_t>(units);
-  p.pad = static_cast<int32_t>((kWave - units % kWave) % kWave);
-  p.per_lane = static_cast<int32_t>((units + p.pad) / kWave);
   // the scales (2 x vecs fp16) close the record; everything before is codes
-  p.code_units = static_cast<int32_t>((record_bytes - 4LL * g.vecs) / 128);
+  const int64_t scale_bytes = 4LL * g.vecs;
+  const int64_t code_units = (record_bytes - scale_bytes) / 128;
+  if (g.vecs % 64 != 0 || code_units % kWave != 0 || scale_bytes % (4 * kWave) != 0)
+    return hipErrorInvalidValue;
+  p.units = static_cast<int32_t>(record_bytes / 128);
+  p.code_units = static_cast<int32_t>(code_units);
+  p.scale_bytes = static_cast<int32_t>(scale_bytes);
   const uint32_t mul_lanes = crc_x8n(static_cast<uint64_t>(128) * kWave);
   for (int k = 0; k < 4; ++k)
     for (int i = 0; i < 8; ++i) p.m_basis[k][i] = crc_mulmod(1u << (8 * k + i), mul_lanes);
-  for (int k = 0; k < 6; ++k) p.shift[k] = crc_x8n(static_cast<uint64_t>(128) << k);
+  for (int i = 0; i < kWave; ++i) {
+    const uint64_t back = static_cast<uint64_t>(kWave - 1 - i);
+    p.code_shift[i] = crc_x8n(128 * back + static_cast<uint64_t>(scale_bytes));
+    p.scale_shift[i] = crc_x8n(static_cast<uint64_t>(scale_bytes / kWave) * back);
+  }
   p.init_term = crc_mulmod(0xFFFFFFFFu, crc_x8n(static_cast<uint64_t>(record_bytes)));
   const unsigned groups =
       static_cast<unsigned>((p.n_records + kRecordsPerGroup - 1) / kRecordsPerGroup);

@@ -11,12 +11,13 @@
 //   raw(A || B) = raw(A) * x^(8|B|) mod P  xor  raw(B),
 // and the standard CRC is ~(0xFFFFFFFF * x^(8|M|) mod P  xor  raw(M)).
 // One wave handles one record: lane i feeds its contiguous chunk of
-// `chunk` bytes into a zero register, a word per three table lookups, then
-// the 64 lane values are merged pairwise in 6 rounds, round k shifting the
-// left half by x^(8 * chunk * 2^k).  Leading zero bytes leave a zero
-// register unchanged, so a record shorter than 64 * chunk is handled by
-// treating it as preceded by `pad` zero bytes.  The shift constants depend
-// only on the record size and are computed once per launch on the host.
+// `chunk` bytes into a zero register, a word per three table lookups; the
+// chunk is followed by 63 - i chunks, so lane i multiplies its value by
+// x^(8 * chunk * (63 - i)) and the record's raw CRC is the xor of the 64
+// products.  Leading zero bytes leave a zero register unchanged, so a record
+// shorter than 64 * chunk is handled by treating it as preceded by `pad` zero
+// bytes.  The 64 constants depend only on the record size and are computed
+// once per launch on the host.
 #include "crc_device.h"
 #include "hkv_device.h"
 #include "hkv_launch.h"
@@ -35,7 +36,7 @@ struct CrcParams {
   int32_t chunk;         // bytes per lane (multiple of 4)
   int32_t pad;           // 64 * chunk - record bytes
   int32_t aligned;       // chunk and pad multiples of 16
-  uint32_t shift[6];     // x^(8 * chunk * 2^k) mod P, reflected
+  uint32_t lane_shift[kWave];   // x^(8 * chunk * (63 - i)) mod P, reflected
   uint32_t init_term;    // 0xFFFFFFFF * x^(8 * record bytes) mod P
 };
 
@@ -126,14 +127,10 @@ __global__ __launch_bounds__(kThreads) void crc32_kernel(CrcParams p) {
       crc = feed_word(T0, T1, T2, crc, *reinterpret_cast<const uint32_t*>(base + u));
   }
 
+  // lane i's chunk is followed by 63 - i chunks
+  crc = crc_mulmod(crc, p.lane_shift[lane]);
 #pragma unroll
-  for (int k = 0; k < 6; ++k) {
-    const uint32_t other = __shfl_xor(crc, 1 << k);
-    const bool left = ((lane >> k) & 1) == 0;
-    const uint32_t lo = left ? crc : other;     // earlier bytes
-    const uint32_t hi = left ? other : crc;
-    crc = crc_mulmod(lo, p.shift[k]) ^ hi;
-  }
+  for (int k = 0; k < 6; ++k) crc ^= __shfl_xor(crc, 1 << k);
   if (lane == 0) p.out[r] = ~(p.init_term ^ crc);
 }
 
@@ -239,7 +236,8 @@ hipError_t launch_crc32(const Geometry& g, int64_t record_bytes, const RecordVie
   p.chunk = static_cast<int32_t>(chunk);
   p.pad = static_cast<int32_t>(kWave * chunk - record_bytes);
   p.aligned = aligned ? 1 : 0;
-  for (int k = 0; k < 6; ++k) p.shift[k] = crc_x8n(static_cast<uint64_t>(chunk) << k);
+  for (int i = 0; i < kWave; ++i)
+    p.lane_shift[i] = crc_x8n(static_cast<uint64_t>(chunk) * static_cast<uint64_t>(kWave - 1 - i));
   p.init_term = crc_mulmod(0xFFFFFFFFu, crc_x8n(static_cast<uint64_t>(record_bytes)));
   const unsigned groups =
       static_cast<unsigned>((p.n_records + kRecordsPerGroup - 1) / kRecordsPerGroup);

@@ -148,9 +148,10 @@ int hkv_quant_int4(const hkv_shape* shape, const hkv_pages* src, int32_t src_dty
  * equal to what hkv_crc32_blocks computes over them.  Entries of skipped
  * blocks are left unchanged by the one-pass path; the two-pass fallback
  * (below) writes the CRC of whatever those records hold.  The put kernel
- * stages each workgroup's codes
- * and scales in LDS and stores the raw CRC of every 128-byte unit of the
- * record to `workspace`; a second kernel merges them per record.
+ * stages each workgroup's codes in LDS and stores the raw CRC of every
+ * 128-byte unit of the record's codes to `workspace`; a second kernel reads
+ * each record's scales back and merges both into the record's CRC.  The
+ * workspace's contents on entry do not matter and are left undefined.
  * workspace: 16-byte aligned device memory of at least
  * hkv_quant_crc_workspace_bytes() bytes (4 bytes per 128 bytes of records);
  * when block_tokens * n_kv_heads is not a multiple of 64 that is 0, no

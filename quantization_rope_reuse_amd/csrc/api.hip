@@ -45,8 +45,8 @@ int check_shape(const hkv_shape* s, Geometry* g) {
   g->block_tokens = s->block_tokens;
   g->n_heads = s->n_kv_heads;
   g->vecs = static_cast<int32_t>(vecs);
-  const int64_t per_wg = hkv::kFetchMinGroupVecs < hkv::kQuantGroupVecs ? hkv::kFetchMinGroupVecs
-                                                                         : hkv::kQuantGroupVecs;
+  // the smallest chunk any kernel uses bounds the workgroup count
+  const int64_t per_wg = hkv::kFetchMinGroupVecs;
   const int64_t chunks = (vecs + per_wg - 1) / per_wg;
   if (static_cast<int64_t>(s->n_blocks) * 2 * chunks > INT32_MAX) return HKV_ERR_UNSUPPORTED;
   return HKV_OK;

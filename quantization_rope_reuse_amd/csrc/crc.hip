@@ -159,30 +159,19 @@ struct MergeParams {
   int32_t code_units;          // multiple of 64
   int32_t scale_bytes;         // multiple of 256
   uint32_t m_basis[4][8];      // (1 << (8k + i)) * x^(8 * 128 * 64) mod P
+  uint32_t t_basis[4][8];      // (1 << i) * x^(8 * (s + 1)) mod P: the byte tables T
   uint32_t code_shift[kWave];  // x^(8*128*(63-i) + 8*scale_bytes) mod P
   uint32_t scale_shift[kWave]; // x^(8*(scale_bytes/64)*(63-i)) mod P
   uint32_t init_term;          // 0xFFFFFFFF * x^(8 * record bytes) mod P
 };
 
-__global__ __launch_bounds__(kThreads) void crc32_merge_kernel(MergeParams p) {
-  __shared__ uint32_t M[4][256];                 // M[k][b] = (b at byte k) * x^(8*128*64)
-  __shared__ uint32_t T[4][256];
-  const int tid = threadIdx.x;
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    uint32_t m = 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) m ^= p.m_basis[k][i] & (0u - ((static_cast<uint32_t>(tid) >> i) & 1u));
-    M[k][tid] = m;
-  }
-  build_crc_tables(T);                           // ends with a barrier
-  const int lane = tid & (kWave - 1);
-  const int r = blockIdx.x * kRecordsPerGroup + tid / kWave;
-  if (r >= p.n_records) return;                 // whole wave, after the barriers
+// One record's CRC in one wave (see above).
+__device__ __forceinline__ void merge_record(const MergeParams& p, const uint32_t (*M)[256],
+                                             const uint32_t (*T)[256], int r, int lane) {
   const int layer = r / p.n_blocks;
   const int blk = r - layer * p.n_blocks;
   const int page = p.table[blk];
-  if (page < 0 || page >= p.num_pages) return;
+  if (page < 0 || page >= p.num_pages) return;   // whole wave
   const uint32_t* part = p.partials + static_cast<int64_t>(r) * p.units + lane;
   const int per_lane = p.scale_bytes / kWave;    // bytes, a multiple of 4
   const uint32_t* sc = reinterpret_cast<const uint32_t*>(
@@ -213,6 +202,29 @@ __global__ __launch_bounds__(kThreads) void crc32_merge_kernel(MergeParams p) {
 #pragma unroll
   for (int k = 0; k < 6; ++k) v ^= __shfl_xor(v, 1 << k);
   if (lane == 0) p.out[r] = ~(p.init_term ^ v);
+}
+
+// One wave per record (several records per wave measured slower).
+__global__ __launch_bounds__(kThreads) void crc32_merge_kernel(MergeParams p) {
+  __shared__ uint32_t M[4][256];                 // M[k][b] = (b at byte k) * x^(8*128*64)
+  __shared__ uint32_t T[4][256];                 // T[s][b] = b * x^(8(s+1))
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    uint32_t m = 0, t = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t bit = 0u - ((static_cast<uint32_t>(tid) >> i) & 1u);
+      m ^= p.m_basis[k][i] & bit;
+      t ^= p.t_basis[k][i] & bit;
+    }
+    M[k][tid] = m;
+    T[k][tid] = t;
+  }
+  __syncthreads();
+  const int r = blockIdx.x * kRecordsPerGroup + tid / kWave;
+  if (r >= p.n_records) return;                  // whole wave, after the barrier
+  merge_record(p, M, T, r, tid & (kWave - 1));
 }
 
 }  // namespace
@@ -269,6 +281,9 @@ hipError_t launch_crc32_merge(const Geometry& g, int64_t record_bytes, const Rec
   const uint32_t mul_lanes = crc_x8n(static_cast<uint64_t>(128) * kWave);
   for (int k = 0; k < 4; ++k)
     for (int i = 0; i < 8; ++i) p.m_basis[k][i] = crc_mulmod(1u << (8 * k + i), mul_lanes);
+  for (int s = 0; s < 4; ++s)
+    for (int i = 0; i < 8; ++i)
+      p.t_basis[s][i] = crc_mulmod(1u << i, crc_x8n(static_cast<uint64_t>(s + 1)));
   for (int i = 0; i < kWave; ++i) {
     const uint64_t back = static_cast<uint64_t>(kWave - 1 - i);
     p.code_shift[i] = crc_x8n(128 * back + static_cast<uint64_t>(scale_bytes));

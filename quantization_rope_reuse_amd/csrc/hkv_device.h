@@ -21,8 +21,6 @@ constexpr int kThreads = 256;                          // 4 waves per workgroup
 constexpr int kVecsPerWave = kWave / kLanesPerVec;     // 8
 constexpr int kVecsPerPass = kThreads / kLanesPerVec;  // 32
 constexpr int kFetchMinGroupVecs = kVecsPerWave * (kThreads / kWave);  // 32: smallest fetch chunk
-constexpr int kQuantPasses = 2;                        // put: passes per wave
-constexpr int kQuantGroupVecs = kVecsPerWave * kQuantPasses * (kThreads / kWave);   // 64
 
 enum DType { kF32 = 0, kF16 = 1, kBF16 = 2 };
 enum Format { kFP8 = 0, kINT4 = 1 };

@@ -203,13 +203,18 @@ def test_large_blocks(fmt):
 
 
 @pytest.mark.parametrize("fmt", ["fp8", "int4"])
-@pytest.mark.parametrize("shape", [(16, 8, 2, 5), (64, 8, 1, 3), (37, 9, 2, 4), (8, 16, 3, 6)],
-                         ids=["16x8", "64x8", "37x9_fallback", "8x16"])
+@pytest.mark.parametrize("shape", [(16, 8, 2, 5), (64, 8, 1, 3), (37, 9, 2, 4), (8, 16, 3, 6),
+                                   (24, 8, 2, 4), (8, 8, 2, 5)],
+                         ids=["16x8", "64x8", "37x9_fallback", "8x16", "24x8_two_pass",
+                              "8x8_two_pass"])
 def test_fused_put_crc(fmt, shape):
     """Put and CRC in one pass: the records equal the separate put's, the CRCs
     equal the oracle's for every written block, and the entries of skipped
-    blocks stay as they were.  37 x 9 = 333 vectors per block is not a
-    multiple of 64: that shape runs the put and the CRC kernel."""
+    blocks stay as they were.  Blocks of 128k vectors run the put's four-pass
+    chunks (128 vectors); 24 x 8 = 192 and 8 x 8 = 64 vectors its two-pass
+    chunks (64), and give the merge 3 and 1 scale words per lane.  37 x 9 =
+    333 vectors per block is not a multiple of 64: that shape runs the put and
+    the CRC kernel."""
     tb, H, L, P = shape
     print(f"[small] fused put+crc {fmt} {shape}", flush=True)
     rng = np.random.default_rng(71)

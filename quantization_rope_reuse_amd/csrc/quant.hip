@@ -182,9 +182,9 @@ __device__ __forceinline__ uint32_t quant_vector(float (&a)[8], float (&b)[8], u
 // zero CRC register (byte tables in LDS) and stores that raw value in
 // `partials` at the unit's index in the record.  The byte tables are built
 // while the source loads are in flight.  The scale units at the end of the
-// record are left to the merge kernel (crc.hip), which reads them back: a
-// 65th thread here would run a whole second wave's chain for one unit, and
-// measured 8% slower.
+// record are left to the merge kernel (crc.hip), which reads them back: one
+// more thread here for the chunk's scale unit would run a whole further
+// wave's chain for one unit (measured 8% slower with chunks of 64).
 template <int FMT, int SDT, bool CRC, int PASSES>
 __global__ __launch_bounds__(kThreads) void quant_kernel(QuantParams p) {
   const int layer = blockIdx.y;

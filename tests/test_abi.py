@@ -336,3 +336,14 @@ def test_stream_probe_rejects_bad_arguments():
     assert call(src=0) == H.ERR_INVALID_ARG
     assert call(dst=FAKE + 8) == H.ERR_INVALID_ARG
     assert call(n=0, src=0, dst=0) == H.OK
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    """No fallback: with the shared library absent every call raises instead
+    of computing anything another way."""
+    monkeypatch.setattr(hkv, "LIB_PATH", str(tmp_path / "libhkv_absent.so"))
+    monkeypatch.setattr(hkv, "_lib", None)
+    with pytest.raises(ImportError, match="not built"):
+        hkv.lib()
+    with pytest.raises(ImportError):
+        hkv.record_bytes("fp8", 64, 8)

@@ -50,6 +50,7 @@ struct FetchParams {
   int64_t o_layer, o_page, o_token, o_head;
   int32_t num_pages;
   int32_t n_heads;
+  float rcp_heads;           // 1 / n_heads in fp32, for divmod_small
   int32_t vecs;
   int32_t chunks;
   int32_t vecs_per_chunk;
@@ -141,7 +142,7 @@ __device__ __forceinline__ int pair_of(int sub, int j) {
 // that lanes past the end of the chunk read a valid delta whose result they
 // then discard.
 __device__ __forceinline__ int token_delta(const FetchParams& p, int blk, int v) {
-  const int t = min(v / p.n_heads, p.block_tokens - 1);
+  const int t = min(divmod_small(v, p.n_heads, p.rcp_heads).q, p.block_tokens - 1);
   return p.delta[static_cast<int64_t>(blk) * p.block_tokens + t];
 }
 
@@ -272,8 +273,9 @@ __global__ __launch_bounds__(kThreads) void fetch_kernel(FetchParams p) {
           for (int j = 0; j < 8; ++j) rot(a[j], b[j], cs[j], sn[j]);
         }
       }
-      const int t = v / p.n_heads;
-      const int h = v - t * p.n_heads;
+      const DivMod th = divmod_small(v, p.n_heads, p.rcp_heads);
+      const int t = th.q;
+      const int h = th.r;
       char* dst = out + t * p.o_token + h * p.o_head + 8 * sub * ES;
       store8<ODT, true>(dst, a);
       store8<ODT, true>(dst + 64 * ES, b);
@@ -353,6 +355,7 @@ hipError_t launch_fetch(int fmt, int dst_dtype, int pairs, const Geometry& g,
   p.o_head = dst.head;
   p.num_pages = dst.num_pages;
   p.n_heads = g.n_heads;
+  p.rcp_heads = 1.0f / static_cast<float>(g.n_heads);
   p.vecs = g.vecs;
   for (int i = 0; i < kHeadDim / 2; ++i)
     p.theta[i] = 1.0 / pow(rope_base, static_cast<double>(2 * i) / kHeadDim);

@@ -39,6 +39,27 @@ template <> struct ElemSize<kBF16> { static constexpr int value = 2; };
 // Scalar conversions
 // ---------------------------------------------------------------------------
 
+// Quotient and remainder of v / d for 0 <= v <= 2^24 + 64 and 1 <= d <= 2^24,
+// given rcp = 1/d rounded to fp32 (computed once on the host).  Rounding v,
+// rcp and the product each move v * rcp by at most half an ulp, which keeps
+// the truncated estimate within one of the quotient, and one correction each
+// way makes it exact -- about 8 instructions instead of a 32-bit division.
+struct DivMod {
+  int q, r;
+};
+__device__ __forceinline__ DivMod divmod_small(int v, int d, float rcp) {
+  int q = static_cast<int>(static_cast<float>(v) * rcp);
+  int r = v - q * d;
+  if (r < 0) {
+    --q;
+    r += d;
+  } else if (r >= d) {
+    ++q;
+    r -= d;
+  }
+  return {q, r};
+}
+
 __device__ __forceinline__ float f16_bits_to_f32(uint32_t h) {
   _Float16 x = __builtin_bit_cast(_Float16, static_cast<uint16_t>(h));
   return static_cast<float>(x);                       // exact

@@ -35,6 +35,7 @@ struct QuantParams {
   uint8_t* rec;
   int64_t rec_layer, rec_block;
   int32_t n_heads;
+  float rcp_heads;       // 1 / n_heads in fp32, for divmod_small
   int32_t vecs;
   int32_t chunks;
   int32_t vecs_per_chunk;
@@ -226,8 +227,9 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(QuantParams p) {
     for (int i = 0; i < kBatch; ++i) {
       const int v = v0 + kVecsPerWave * (i0 + i) + vsub;
       if (v < v_end) {
-        const int t = v / p.n_heads;
-        const int h = v - t * p.n_heads;
+        const DivMod th = divmod_small(v, p.n_heads, p.rcp_heads);
+        const int t = th.q;
+        const int h = th.r;
         const char* x_ptr = src + t * p.s_token + h * p.s_head + 8 * sub * ES;
         ra[i] = load_run<SDT>(x_ptr);
         rb[i] = load_run<SDT>(x_ptr + 64 * ES);
@@ -323,6 +325,7 @@ QuantParams make_params(const Geometry& g, const PageView& src, const int32_t* t
   p.rec_layer = dst.layer;
   p.rec_block = dst.block;
   p.n_heads = g.n_heads;
+  p.rcp_heads = 1.0f / static_cast<float>(g.n_heads);
   p.vecs = g.vecs;
   p.chunks = 0;                 // set per pass count at launch
   p.vecs_per_chunk = 0;

@@ -1,5 +1,6 @@
 """The C ABI under HIP graph capture: put, CRC, page order, per-layer fetch,
-per-token fetch, drift and top-k selection recorded once into a graph
+per-token fetch, drift, top-k selection and the fused INT4 put + CRC
+recorded once into a graph
 (torch.cuda.CUDAGraph) and replayed.  The calls allocate nothing and do not
 synchronize, so they can be captured; every replay must reproduce the eager
 results bit for bit.  Between replays the outputs are scribbled over and other
@@ -41,6 +42,10 @@ def test_graph_capture_and_replay():
     # static buffers, allocated before capture
     rec = hkv.alloc_records(L, nb, "fp8", tb, H, device=DEV)
     crc = torch.empty((L, nb), dtype=torch.int32, device=DEV)
+    rec4 = hkv.alloc_records(L, nb, "int4", tb, H, device=DEV)      # fused put + CRC
+    crc4 = torch.empty((L, nb), dtype=torch.int32, device=DEV)
+    ws4 = torch.empty(hkv.quant_crc_workspace_bytes("int4", L, nb, tb, H), dtype=torch.uint8,
+                      device=DEV)
     order = torch.empty(nb, dtype=torch.int32, device=DEV)
     ok = torch.empty((L, nb, tb, H, 128), dtype=torch.bfloat16, device=DEV)
     ov = torch.empty_like(ok)
@@ -49,7 +54,7 @@ def test_graph_capture_and_replay():
     drift = torch.empty(dw.n_tokens, dtype=torch.float32, device=DEV)
     sel = torch.empty(k_sel, dtype=torch.int32, device=DEV)
     ws = torch.empty(hkv.select_workspace_bytes(dw.n_tokens), dtype=torch.uint8, device=DEV)
-    outs = (rec, crc, order, ok, ov, tk, tv, drift, sel)
+    outs = (rec, crc, order, ok, ov, tk, tv, drift, sel, rec4, crc4)
 
     def step(stream=None):
         hkv.quant_fp8(kp, vp, put_tab, rec, stream=stream)
@@ -63,6 +68,7 @@ def test_graph_capture_and_replay():
                                             tk, tv, stream=stream)
         hkv.token_drift(hc, hf, out=drift, stream=stream)
         hkv.select_top_tokens(drift, k_sel, out=sel, workspace=ws, stream=stream)
+        hkv.quant_crc("int4", kp, vp, put_tab, rec4, crc_out=crc4, workspace=ws4, stream=stream)
 
     step()
     torch.cuda.synchronize()
@@ -85,10 +91,14 @@ def test_graph_capture_and_replay():
         torch.cuda.synchronize()
         del junk
         for name, got, want in zip(("records", "crc", "order", "fetch K", "fetch V",
-                                    "per-token K", "per-token V", "drift", "selection"),
+                                    "per-token K", "per-token V", "drift", "selection",
+                                    "fused INT4 records", "fused INT4 CRC"),
                                    outs, eager):
             assert torch.equal(got.view(torch.uint8), want.view(torch.uint8)), \
                 f"replay {replay}: {name} differs from the eager run"
     # and the eager run itself against the oracle's selection on its drift
     assert np.array_equal(eager[8].cpu().numpy(), O.select_top_tokens(eager[7].cpu().numpy(),
                                                                      k_sel))
+    # and the fused INT4 CRCs against the oracle's CRC of the records written
+    got = eager[10].cpu().numpy().view(np.uint32)
+    assert np.array_equal(got, O.crc32_records(eager[9].cpu().numpy()))

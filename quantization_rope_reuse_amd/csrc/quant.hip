@@ -223,17 +223,16 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(QuantParams p) {
 #pragma unroll
   for (int i0 = 0; i0 < PASSES; i0 += kBatch) {
     RawSrc<SDT> ra[kBatch], rb[kBatch];
+    // Unconditional loads: lanes past the chunk's end load its last vector,
+    // whose amax they compute for nothing and whose codes they do not store
+    // (no zero fill, no branch around the conversion).
 #pragma unroll
     for (int i = 0; i < kBatch; ++i) {
-      const int v = v0 + kVecsPerWave * (i0 + i) + vsub;
-      if (v < v_end) {
-        const DivMod th = divmod_small(v, p.n_heads, p.rcp_heads);
-        const int t = th.q;
-        const int h = th.r;
-        const char* x_ptr = src + t * p.s_token + h * p.s_head + 8 * sub * ES;
-        ra[i] = load_run<SDT>(x_ptr);
-        rb[i] = load_run<SDT>(x_ptr + 64 * ES);
-      }
+      const int v = min(v0 + kVecsPerWave * (i0 + i) + vsub, v_end - 1);
+      const DivMod th = divmod_small(v, p.n_heads, p.rcp_heads);
+      const char* x_ptr = src + th.q * p.s_token + th.r * p.s_head + 8 * sub * ES;
+      ra[i] = load_run<SDT>(x_ptr);
+      rb[i] = load_run<SDT>(x_ptr + 64 * ES);
     }
     if constexpr (CRC) {
       if (i0 == 0) build_crc_tables(T);        // every thread; ends with a barrier
@@ -243,13 +242,8 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(QuantParams p) {
       const int v = v0 + kVecsPerWave * (i0 + i) + vsub;
       const bool active = v < v_end;
       float a[8], b[8];
-      if (active) {
-        run_to_f32<SDT>(ra[i], a);
-        run_to_f32<SDT>(rb[i], b);
-      } else {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) a[j] = b[j] = 0.0f;
-      }
+      run_to_f32<SDT>(ra[i], a);
+      run_to_f32<SDT>(rb[i], b);
       const uint32_t sbits = quant_vector<FMT, CRC>(a, b, codes + static_cast<int64_t>(v) * CB,
                                                     sub, active, stage + (v - chunk_v0) * CB);
       // lane 8*(i0+i) + r keeps the scale of vector r of this pass

@@ -19,7 +19,6 @@ constexpr int kLanesPerVec = 8;
 constexpr int kWave = 64;
 constexpr int kThreads = 256;                          // 4 waves per workgroup
 constexpr int kVecsPerWave = kWave / kLanesPerVec;     // 8
-constexpr int kVecsPerPass = kThreads / kLanesPerVec;  // 32
 constexpr int kFetchMinGroupVecs = kVecsPerWave * (kThreads / kWave);  // 32: smallest fetch chunk
 
 enum DType { kF32 = 0, kF16 = 1, kBF16 = 2 };

@@ -243,6 +243,36 @@ def test_fused_put_crc(fmt, shape):
             assert (got[:, b] == 0x1234567).all(), f"skipped block {b} CRC was written"
 
 
+@pytest.mark.parametrize("fmt", ["fp8", "int4"])
+@pytest.mark.parametrize("src_dtype", ["f32", "f16"])
+def test_fused_put_crc_other_sources(fmt, src_dtype):
+    """The fused put + CRC from fp32 (two load batches per wave in the
+    four-pass chunks; the CRC tables are built during the first) and fp16
+    sources: records equal to the separate put's, CRCs equal to the oracle's."""
+    tb, H, L, P = 16, 8, 2, 5
+    print(f"[small] fused put+crc {fmt} from {src_dtype}", flush=True)
+    rng = np.random.default_rng(75)
+    kp = rng.standard_normal((L, P, tb, H, 128)).astype(np.float32)
+    vp = (rng.standard_normal((L, P, tb, H, 128)) * 3).astype(np.float32)
+    table = np.array([2, 0, -1, 4, 1, 3], dtype=np.int32)
+    rec, ref, live = _put_both(kp, vp, table, fmt, src_dtype)
+    tdt = TORCH_OF[src_dtype]
+    rec2 = hkv.alloc_records(L, len(table), fmt, tb, H, device=DEV)
+    rec2.fill_(0xA5)
+    crc = torch.full((L, len(table)), 0x1234567, dtype=torch.int32, device=DEV)
+    hkv.quant_crc(fmt, torch.from_numpy(kp).to(DEV, tdt), torch.from_numpy(vp).to(DEV, tdt),
+                  _dev_i32(table), rec2, crc_out=crc)
+    torch.cuda.synchronize()
+    assert torch.equal(rec2, rec), "fused put wrote different records"
+    got = crc_u32(crc)
+    want = O.crc32_records(ref)
+    for b in range(len(table)):
+        if live[b]:
+            assert np.array_equal(got[:, b], want[:, b]), f"block {b} CRC"
+        else:
+            assert (got[:, b] == 0x1234567).all(), f"skipped block {b} CRC was written"
+
+
 def test_stream_probe_pattern():
     """The measurement aid's output: every 16-byte unit i of the source lands
     at output unit (i // 8) * 16 + i % 8 and, xor 0x5A5A5A5A, 8 units later."""

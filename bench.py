@@ -745,10 +745,10 @@ def overlap(a, w, L, hkv, rec_l, ok_l, ov_l, ftab, dm, order, side):
 
 def cpu_baseline(w, records_bytes, budget_s):
     """The CPU oracle, as it stands, on a bounded sample of the same workload:
-    put + CRC + fetch of the first n blocks of a layer, n doubled until one
-    run takes about a third of `budget_s`, then whole layers added while the
-    total stays under `budget_s`.  Reported in GB/s of the same algorithmic
-    bytes as the GPU figures."""
+    put + CRC + fetch of the first n blocks of a layer, n sized from a short
+    calibration run so that the measured run takes about 0.8 * `budget_s`
+    (whole layers are added when one layer is not enough).  Reported in GB/s
+    of the same algorithmic bytes as the GPU figures."""
     import numpy as np
 
     import oracle as O
@@ -773,11 +773,10 @@ def cpu_baseline(w, records_bytes, budget_s):
         O.fetch(rec, O.FMT_FP8, tb, H, table, dm_all[:n], w.rope_base, w.pairs, ko, vo, "bf16")
         return time.perf_counter() - t0, time.process_time() - c0
 
-    n = 4
-    wall, cpu_t = run(0, n)
-    while wall < budget_s / 3 and n < nb:
-        n = min(nb, max(n * 2, int(n * budget_s / 3 / max(wall, 1e-3))))
-        wall, cpu_t = run(0, n)
+    n = 32                                      # calibration: per-block time
+    wall, _ = run(0, n)
+    n = min(nb, max(1, int(n * 0.8 * budget_s / max(wall, 1e-3))))
+    wall, cpu_t = run(0, n)                     # the measured sample
     blocks, layers = n, 1
     while n == nb and wall * (layers + 1) / layers < budget_s and layers < w.n_layers:
         wl, cl = run(layers, nb)

@@ -745,8 +745,8 @@ def overlap(a, w, L, hkv, rec_l, ok_l, ov_l, ftab, dm, order, side):
 
 def cpu_baseline(w, records_bytes, budget_s):
     """The CPU oracle, as it stands, on a bounded sample of the same workload:
-    put + CRC + fetch of the first n blocks of a layer, n sized from a short
-    calibration run so that the measured run takes about 0.8 * `budget_s`
+    put + CRC + fetch of the first n blocks of a layer, n sized from two short
+    calibration runs so that the measured run takes about 0.8 * `budget_s`
     (whole layers are added when one layer is not enough).  Reported in GB/s
     of the same algorithmic bytes as the GPU figures."""
     import numpy as np
@@ -773,9 +773,12 @@ def cpu_baseline(w, records_bytes, budget_s):
         O.fetch(rec, O.FMT_FP8, tb, H, table, dm_all[:n], w.rope_base, w.pairs, ko, vo, "bf16")
         return time.perf_counter() - t0, time.process_time() - c0
 
-    n = 32                                      # calibration: per-block time
-    wall, _ = run(0, n)
-    n = min(nb, max(1, int(n * 0.8 * budget_s / max(wall, 1e-3))))
+    # calibration: fixed and per-block time from two short runs
+    t32, _ = run(0, 32)
+    t128, _ = run(0, 128)
+    per_block = max((t128 - t32) / 96, 1e-6)
+    fixed = max(t32 - 32 * per_block, 0.0)
+    n = min(nb, max(1, int((0.8 * budget_s - fixed) / per_block)))
     wall, cpu_t = run(0, n)                     # the measured sample
     blocks, layers = n, 1
     while n == nb and wall * (layers + 1) / layers < budget_s and layers < w.n_layers:

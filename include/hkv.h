@@ -76,7 +76,10 @@ typedef enum { HKV_ROPE_INTERLEAVED = 0, HKV_ROPE_HALF_SPLIT = 1 } hkv_rope_pair
 #define HKV_HEAD_DIM 128
 
 /* Geometry shared by all calls.  A "vector" is one (layer, K|V, token, head)
- * row of head_dim elements. */
+ * row of head_dim elements.  Calls return HKV_ERR_UNSUPPORTED for shapes
+ * beyond the launch grids: n_layers > 65535, block_tokens * n_kv_heads >
+ * 2^24, n_layers * n_blocks > 2^31 - 1, or n_blocks * 2 *
+ * ceil(block_tokens * n_kv_heads / 16) > 2^31 - 1. */
 typedef struct {
   int32_t n_layers;      /* >= 0 */
   int32_t n_blocks;      /* >= 0, logical blocks per layer */

@@ -10,11 +10,12 @@
 // follow the KV-handoff module ("Модуль 13: KV-хэндофф: передача кеша между
 // моделями и узлами"), module13.py listing, rope_cache / apply_rope.
 //
-// Work decomposition: one workgroup (4 waves) per (layer, block, K|V, chunk of
+// Work decomposition: one workgroup per (layer, block, K|V, chunk of
 // vectors); each wave owns 8 consecutive vectors per pass, 8 lanes per
-// vector, and makes one pass (FP8 with per-block deltas: chunks of 32
-// vectors) or two (INT4, per-token deltas: chunks of 64).  Small workgroups
-// measured best on MI355X (about 33k workgroups per Llama-3-70B-shaped layer).  Every lane
+// vector.  FP8 with per-block deltas: one pass, 4 waves per workgroup
+// (chunks of 32 vectors, about 33k workgroups per Llama-3-70B-shaped layer);
+// INT4 and per-token deltas: two passes, one wave per workgroup (chunks of
+// 16).  Every lane
 // of a key workgroup needs 8 (cos, sin) pairs; the 64 lanes of a wave first
 // compute one pair each (i = lane) in double precision and then gather the 8
 // they need with cross-lane reads, so the angle setup costs one double sincos
@@ -178,8 +179,8 @@ __device__ __forceinline__ void token_angles(const FetchParams& p, int dm, doubl
 // its own token's delta.  When the head count is a multiple of 8 the 8
 // vectors of a pass belong to one token and lane i computes pair i's angle
 // once per pass; otherwise each lane computes the 8 angles it needs.
-template <int FMT, int ODT, int PAIRS, bool PER_TOKEN, int PASSES>
-__global__ __launch_bounds__(kThreads) void fetch_kernel(FetchParams p) {
+template <int FMT, int ODT, int PAIRS, bool PER_TOKEN, int PASSES, int THREADS>
+__global__ __launch_bounds__(THREADS) void fetch_kernel(FetchParams p) {
   const int layer = blockIdx.y;
   const int chunk = blockIdx.x % p.chunks;
   const int bk = blockIdx.x / p.chunks;
@@ -283,30 +284,39 @@ __global__ __launch_bounds__(kThreads) void fetch_kernel(FetchParams p) {
   }
 }
 
-// Passes per wave, measured on MI355X: per-block-delta FP8 fetches are
-// fastest with one pass (8 vectors per wave, 32 per workgroup); INT4 records
-// (half the bytes per vector) and per-token deltas (more angle work per
-// vector) need the second pass's loads in flight to cover their latency.
+// Passes per wave and workgroup size, measured on MI355X: per-block-delta
+// FP8 fetches are fastest with one pass (8 vectors per wave) in workgroups of
+// 4 waves (32 vectors); INT4 records (half the bytes per vector) and
+// per-token deltas (more angle work per vector) need the second pass's loads
+// in flight to cover their latency, and run 2-3% faster in one-wave
+// workgroups (16 vectors) than in four-wave ones.
 template <int FMT, bool PT>
 constexpr int fetch_passes() {
   return (FMT == kFP8 && !PT) ? 1 : 2;
 }
+template <int FMT, bool PT>
+constexpr int fetch_threads() {
+  return (FMT == kFP8 && !PT) ? 4 * kWave : kWave;
+}
+static_assert(kVecsPerWave * 2 >= kFetchMinGroupVecs,
+              "the shape check bounds the chunk count with the smallest fetch chunk");
 
-template <int FMT, int ODT, int PAIRS, bool PT, int PASSES>
-hipError_t launch_passes(FetchParams p, const Geometry& g, hipStream_t stream) {
-  // Workgroups of 4 waves x PASSES x 8 vectors.
-  p.vecs_per_chunk = kVecsPerWave * PASSES * (kThreads / kWave);
+template <int FMT, int ODT, int PAIRS, bool PT, int PASSES, int THREADS>
+hipError_t launch_shape(FetchParams p, const Geometry& g, hipStream_t stream) {
+  // Workgroups of THREADS / 64 waves x PASSES x 8 vectors.
+  p.vecs_per_chunk = kVecsPerWave * PASSES * (THREADS / kWave);
   p.chunks = (g.vecs + p.vecs_per_chunk - 1) / p.vecs_per_chunk;
   dim3 grid(static_cast<unsigned>(g.n_blocks) * 2u * static_cast<unsigned>(p.chunks),
             static_cast<unsigned>(g.n_layers));
-  hipLaunchKernelGGL((fetch_kernel<FMT, ODT, PAIRS, PT, PASSES>), grid, dim3(kThreads), 0, stream,
-                     p);
+  hipLaunchKernelGGL((fetch_kernel<FMT, ODT, PAIRS, PT, PASSES, THREADS>), grid, dim3(THREADS), 0,
+                     stream, p);
   return hipGetLastError();
 }
 
 template <int FMT, int ODT, int PAIRS, bool PT>
 hipError_t launch_t(const FetchParams& p, const Geometry& g, hipStream_t stream) {
-  return launch_passes<FMT, ODT, PAIRS, PT, fetch_passes<FMT, PT>()>(p, g, stream);
+  return launch_shape<FMT, ODT, PAIRS, PT, fetch_passes<FMT, PT>(), fetch_threads<FMT, PT>()>(
+      p, g, stream);
 }
 
 template <int FMT, int ODT, bool PT>

@@ -19,7 +19,7 @@ constexpr int kLanesPerVec = 8;
 constexpr int kWave = 64;
 constexpr int kThreads = 256;                          // 4 waves per workgroup
 constexpr int kVecsPerWave = kWave / kLanesPerVec;     // 8
-constexpr int kFetchMinGroupVecs = kVecsPerWave * (kThreads / kWave);  // 32: smallest fetch chunk
+constexpr int kFetchMinGroupVecs = kVecsPerWave * 2;  // 16: smallest fetch chunk (one wave, two passes)
 
 enum DType { kF32 = 0, kF16 = 1, kBF16 = 2 };
 enum Format { kFP8 = 0, kINT4 = 1 };

@@ -65,7 +65,7 @@ extern "C" {
 typedef enum {
   HKV_OK = 0,
   HKV_ERR_INVALID_ARG = -1,  /* null pointer, bad size, misalignment, bad enum */
-  HKV_ERR_UNSUPPORTED = -2,  /* a well-formed request this build does not do  */
+  HKV_ERR_UNSUPPORTED = -2,  /* a well-formed request the library does not do */
   HKV_ERR_HIP = -3           /* the HIP runtime reported a launch error        */
 } hkv_status;
 

@@ -12,6 +12,7 @@ the library raises.
 from __future__ import annotations
 
 import ctypes
+import functools
 import os
 import re
 
@@ -183,6 +184,25 @@ def _check(call: str, status: int):
         raise HkvError(call, status)
 
 
+def _on_one_gpu(fn):
+    """Every tensor argument of a call must be a GPU tensor and all of them on
+    one device: the kernels dereference their addresses."""
+    @functools.wraps(fn)
+    def checked(*args, **kwargs):
+        dev = None
+        for a in (*args, *kwargs.values()):
+            if isinstance(a, torch.Tensor):
+                if a.device.type != "cuda":
+                    raise ValueError(f"{fn.__name__}: tensor arguments must be on a GPU, "
+                                     f"got one on {a.device}")
+                if dev is None:
+                    dev = a.device
+                elif a.device != dev:
+                    raise ValueError(f"{fn.__name__}: tensor arguments on {dev} and {a.device}")
+        return fn(*args, **kwargs)
+    return checked
+
+
 def alloc_records(n_layers: int, n_blocks: int, fmt, block_tokens: int, n_kv_heads: int,
                   device="cuda"):
     """A uint8 [L, n_blocks, record_bytes] tensor (block stride rounded up to 16)."""
@@ -210,11 +230,13 @@ def _quant(name, k_pages, v_pages, block_table, records, stream):
     return records
 
 
+@_on_one_gpu
 def quant_fp8(k_pages, v_pages, block_table, records, stream=None):
     """Quantize the blocks k/v_pages[:, block_table[b]] into records[:, b] (FP8)."""
     return _quant("hkv_quant_fp8", k_pages, v_pages, block_table, records, stream)
 
 
+@_on_one_gpu
 def quant_int4(k_pages, v_pages, block_table, records, stream=None):
     """Quantize the blocks k/v_pages[:, block_table[b]] into records[:, b] (INT4)."""
     return _quant("hkv_quant_int4", k_pages, v_pages, block_table, records, stream)
@@ -226,6 +248,7 @@ def quant_crc_workspace_bytes(fmt, n_layers: int, n_blocks: int, block_tokens: i
     return int(lib().hkv_quant_crc_workspace_bytes(ctypes.byref(shape), FORMATS[fmt]))
 
 
+@_on_one_gpu
 def quant_crc(fmt, k_pages, v_pages, block_table, records, crc_out=None, workspace=True,
               stream=None):
     """Put (FP8 or INT4) and the CRC-32 of every written record in one pass.
@@ -278,6 +301,7 @@ def _fetch(name, records, fmt, block_table, delta, n_delta, rope_base, pairs, k_
     return k_pages, v_pages
 
 
+@_on_one_gpu
 def fetch_dequant_rope_shift(records, fmt, block_table, delta_m, rope_base, pairs,
                              k_pages, v_pages, visit_order=None, stream=None):
     """Dequantize records[:, b], shift keys by delta_m[b], store at page
@@ -287,6 +311,7 @@ def fetch_dequant_rope_shift(records, fmt, block_table, delta_m, rope_base, pair
                   lambda nb, tb: nb, rope_base, pairs, k_pages, v_pages, visit_order, stream)
 
 
+@_on_one_gpu
 def fetch_dequant_rope_shift_tokens(records, fmt, block_table, delta_m_tokens, rope_base, pairs,
                                     k_pages, v_pages, visit_order=None, stream=None):
     """As fetch_dequant_rope_shift with one delta per token: delta_m_tokens
@@ -296,6 +321,7 @@ def fetch_dequant_rope_shift_tokens(records, fmt, block_table, delta_m_tokens, r
                   visit_order, stream)
 
 
+@_on_one_gpu
 def page_visit_order(block_table, num_pages: int, out=None, stream=None):
     """Blocks listed by increasing destination page (skipped blocks last):
     an int32 tensor [n_blocks] for fetch_dequant_rope_shift's visit_order."""
@@ -330,6 +356,7 @@ class StreamPair:
             self._handles = None
 
 
+@_on_one_gpu
 def crc32_blocks(records, fmt, block_tokens: int, n_kv_heads: int, out=None, stream=None):
     """CRC-32 of every record; returns a uint32-valued int32 tensor [L, n_blocks]
     (use `.view(torch.uint32)` or mask with 0xFFFFFFFF after widening)."""
@@ -346,6 +373,7 @@ def crc32_blocks(records, fmt, block_tokens: int, n_kv_heads: int, out=None, str
     return out
 
 
+@_on_one_gpu
 def token_drift(h_cached, h_fresh, out=None, stream=None):
     """Per-token drift ||h_fresh[t] - h_cached[t]||_2 of two [n_tokens, d_model]
     tensors (same dtype, same row stride, last axis contiguous); returns a
@@ -373,6 +401,7 @@ def select_workspace_bytes(n_tokens: int) -> int:
     return int(lib().hkv_select_workspace_bytes(int(n_tokens)))
 
 
+@_on_one_gpu
 def select_top_tokens(drift, k: int, out=None, workspace=True, stream=None):
     """Indices of the k largest drift values, increasing; int32 tensor [k].
     workspace: True (a device buffer of select_workspace_bytes is allocated
@@ -430,6 +459,7 @@ def _frame_args(frames, fmt, block_tokens, n_kv_heads):
     return shape, _records(frames)
 
 
+@_on_one_gpu
 def frame_headers(frames, fmt, block_tokens: int, n_kv_heads: int, crc, m_old,
                   layer_base: int = 0, stream=None):
     """Write the header of every frame (records and their CRCs already there)."""
@@ -443,6 +473,7 @@ def frame_headers(frames, fmt, block_tokens: int, n_kv_heads: int, crc, m_old,
     return frames
 
 
+@_on_one_gpu
 def frame_verify(frames, fmt, block_tokens: int, n_kv_heads: int, layer_base: int = 0,
                  out=None, stream=None):
     """Verification flags per frame: an int32 tensor [L, n_blocks] (0 = intact)."""
@@ -459,6 +490,7 @@ def frame_verify(frames, fmt, block_tokens: int, n_kv_heads: int, layer_base: in
     return out
 
 
+@_on_one_gpu
 def frame_delta_m(frames, fmt, block_tokens: int, n_kv_heads: int, m_new, out=None,
                   stream=None):
     """Per-block delta m_new - m_old from the first layer's frame headers."""
@@ -475,6 +507,7 @@ def frame_delta_m(frames, fmt, block_tokens: int, n_kv_heads: int, m_new, out=No
     return out
 
 
+@_on_one_gpu
 def stream_probe(src, dst, stream=None):
     """Measurement aid: read src (uint8, a multiple of 128 bytes) and write it
     twice into dst (twice the size) with the fetch's store pattern."""

@@ -347,3 +347,17 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
         hkv.lib()
     with pytest.raises(ImportError):
         hkv.record_bytes("fp8", 64, 8)
+
+
+def test_binding_requires_gpu_tensors():
+    """Host tensors never reach the library: their addresses would be
+    dereferenced by kernels."""
+    import torch
+    k = torch.zeros((1, 4, 16, 8, 128), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="on a GPU"):
+        H.quant_fp8(k, k, torch.arange(4, dtype=torch.int32),
+                    torch.zeros((1, 4, 33280), dtype=torch.uint8))
+    with pytest.raises(ValueError, match="on a GPU"):
+        H.token_drift(torch.zeros((4, 64)), torch.zeros((4, 64)))
+    with pytest.raises(ValueError, match="on a GPU"):
+        H.select_top_tokens(torch.zeros(64), 8)

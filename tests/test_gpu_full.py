@@ -162,6 +162,61 @@ def test_llama3_70b_full_layerwise_side_stream():
     _properties(src_k, src_v, put_tab, out_k, out_v, ftab, rel_v=0.08, rel_norm=0.08)
 
 
+def test_llama3_70b_per_token_deltas_full():
+    """The per-token fetch at the Llama-3-70B shape in the benchmark's launch
+    configuration (one layer per launch on a side stream, blocks in page
+    order), with random deltas per token (some blocks all zero): sampled
+    blocks against the oracle, the whole cache by its properties."""
+    w = W.LLAMA3_70B
+    print(f"[full] {w.name} per-token deltas", flush=True)
+    src_k, src_v, put_tab = _fill_source(w)
+    L, nb, tb, H = w.n_layers, w.n_blocks, w.block_tokens, w.n_kv_heads
+    rec = hkv.alloc_records(L, nb, "fp8", tb, H, device=DEV)
+    hkv.quant_crc("fp8", src_k, src_v, put_tab, rec)
+    rng = np.random.default_rng(86)
+    dmt = rng.integers(-(1 << 20), 1 << 20, size=(nb, tb)).astype(np.int32)
+    zero_blocks = rng.choice(nb, size=4, replace=False)
+    dmt[zero_blocks] = 0
+    ftab_np = W.fetch_table(w)
+    ftab = torch.from_numpy(ftab_np).to(DEV)
+    dmt_dev = torch.from_numpy(dmt).to(DEV)
+    out_k = canary_fill(torch.empty_like(src_k))
+    out_v = canary_fill(torch.empty_like(src_v))
+    side = torch.cuda.Stream()
+    ready = torch.cuda.Event()
+    ready.record(torch.cuda.current_stream())
+    side.wait_event(ready)
+    order = hkv.page_visit_order(ftab, nb, stream=side)
+    for l in range(L):
+        hkv.fetch_dequant_rope_shift_tokens(rec[l:l + 1], "fp8", ftab, dmt_dev, w.rope_base,
+                                            w.pairs, out_k[l:l + 1], out_v[l:l + 1],
+                                            visit_order=order, stream=side)
+    side.synchronize()
+    torch.cuda.synchronize()
+    put_np = put_tab.cpu().numpy()
+    blocks = sorted(set(int(b) for b in rng.choice(nb, size=6, replace=False)) |
+                    {int(zero_blocks[0]), 0, nb - 1})
+    for i, b in enumerate(blocks):
+        l = [0, L - 1, int(rng.integers(L))][i % 3]
+        xk = host_f64(src_k[l, int(put_np[b])]).astype(np.float32)
+        xv = host_f64(src_v[l, int(put_np[b])]).astype(np.float32)
+        kc, ks = O.quant_fp8_vectors(xk)
+        vc, vs = O.quant_fp8_vectors(xv)
+        ref = O.assemble_records(kc, vc, ks, vs)
+        assert np.array_equal(rec[l, b].cpu().numpy(), ref), f"layer {l} block {b} record"
+        kr, vd = O.fetch_exact(ref[None, None], "fp8", tb, H, dmt[b:b + 1], w.rope_base, w.pairs)
+        kd, _ = O.dequant_records(ref[None, None], "fp8", tb, H)
+        page = int(ftab_np[b])
+        kg = host_f64(out_k[l, page])
+        vg = host_f64(out_v[l, page])
+        check_values_exact(vg, O.round_output(vd[0, 0], w.out_dtype), f"layer {l} block {b} V")
+        if not dmt[b].any():
+            check_values_exact(kg, O.round_output(kd[0, 0], w.out_dtype), f"layer {l} block {b} K")
+        else:
+            check_keys(kg, kr[0, 0], kd[0, 0], w.out_dtype, f"layer {l} block {b} K")
+    _properties(src_k, src_v, put_tab, out_k, out_v, ftab, rel_v=0.08, rel_norm=0.08)
+
+
 def test_llama3_70b_tp8_shard():
     """One GPU's tensor-parallel share of the Llama-3-70B-shaped cache: one KV
     head, 64 vectors per block (two 32-vector fetch chunks, one fused put

@@ -1,6 +1,6 @@
 """The C ABI under HIP graph capture: put, CRC, page order, per-layer fetch,
-per-token fetch, drift, top-k selection and the fused INT4 put + CRC
-recorded once into a graph
+per-token fetch, drift, top-k selection, the fused INT4 put + CRC and the
+record frames (headers, verification) recorded once into a graph
 (torch.cuda.CUDAGraph) and replayed.  The calls allocate nothing and do not
 synchronize, so they can be captured; every replay must reproduce the eager
 results bit for bit.  Between replays the outputs are scribbled over and other
@@ -54,7 +54,11 @@ def test_graph_capture_and_replay():
     drift = torch.empty(dw.n_tokens, dtype=torch.float32, device=DEV)
     sel = torch.empty(k_sel, dtype=torch.int32, device=DEV)
     ws = torch.empty(hkv.select_workspace_bytes(dw.n_tokens), dtype=torch.uint8, device=DEV)
-    outs = (rec, crc, order, ok, ov, tk, tv, drift, sel, rec4, crc4)
+    fr = hkv.alloc_frames(L, nb, "fp8", tb, H, device=DEV)          # record frames
+    fcrc = torch.empty((L, nb), dtype=torch.int32, device=DEV)
+    fflags = torch.empty((L, nb), dtype=torch.int32, device=DEV)
+    m_old = torch.from_numpy(W.block_positions(w)[0]).to(DEV)
+    outs = (rec, crc, order, ok, ov, tk, tv, drift, sel, rec4, crc4, fr, fcrc, fflags)
 
     def step(stream=None):
         hkv.quant_fp8(kp, vp, put_tab, rec, stream=stream)
@@ -69,6 +73,10 @@ def test_graph_capture_and_replay():
         hkv.token_drift(hc, hf, out=drift, stream=stream)
         hkv.select_top_tokens(drift, k_sel, out=sel, workspace=ws, stream=stream)
         hkv.quant_crc("int4", kp, vp, put_tab, rec4, crc_out=crc4, workspace=ws4, stream=stream)
+        hkv.quant_fp8(kp, vp, put_tab, hkv.frame_records(fr), stream=stream)
+        hkv.crc32_blocks(hkv.frame_records(fr), "fp8", tb, H, out=fcrc, stream=stream)
+        hkv.frame_headers(fr, "fp8", tb, H, fcrc, m_old, stream=stream)
+        hkv.frame_verify(fr, "fp8", tb, H, out=fflags, stream=stream)
 
     step()
     torch.cuda.synchronize()
@@ -92,7 +100,8 @@ def test_graph_capture_and_replay():
         del junk
         for name, got, want in zip(("records", "crc", "order", "fetch K", "fetch V",
                                     "per-token K", "per-token V", "drift", "selection",
-                                    "fused INT4 records", "fused INT4 CRC"),
+                                    "fused INT4 records", "fused INT4 CRC", "frames",
+                                    "frame CRCs", "frame flags"),
                                    outs, eager):
             assert torch.equal(got.view(torch.uint8), want.view(torch.uint8)), \
                 f"replay {replay}: {name} differs from the eager run"
@@ -102,3 +111,8 @@ def test_graph_capture_and_replay():
     # and the fused INT4 CRCs against the oracle's CRC of the records written
     got = eager[10].cpu().numpy().view(np.uint32)
     assert np.array_equal(got, O.crc32_records(eager[9].cpu().numpy()))
+    # and the frames: every one intact, the same bytes as the oracle's frames
+    assert not eager[13].cpu().numpy().any()
+    want = O.make_frames(eager[0].cpu().numpy(), "fp8", tb, H, W.block_positions(w)[0])
+    got_fr = eager[11].cpu().numpy()
+    assert np.array_equal(got_fr[:, :, :want.shape[2]], want)

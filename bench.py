@@ -299,13 +299,15 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16->fp8->bf16",
+        "dtype": "f32",
         "data": "synthetic N(0,1), generated on the GPU",
         "config": {
             "workload": "Llama-3-70B-shaped KV, one GPU: 80 layers x 8 KV heads x d128 x "
                         "65536 tokens bf16, blocks of 64, FP8 put + CRC32 in one pass + "
                         "layer-by-layer fetch on a side stream, dm=+8192, RoPE base 500000 "
                         "split-halves",
+            "storage": "bf16 pages -> FP8 E4M3 records with fp16 scales -> bf16 pages "
+                       "(arithmetic in fp32; per-block RoPE angles in fp64)",
             "layers": L, "tokens": T, "kv_heads": H, "head_dim": 128, "block_tokens": tb,
             "step_bytes": step_bytes,
         },

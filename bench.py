@@ -310,7 +310,9 @@ def main():
                        "(arithmetic in fp32; per-block RoPE angles in fp64)",
             "layers": L, "tokens": T, "kv_heads": H, "head_dim": 128, "block_tokens": tb,
             "step_bytes": step_bytes,
+            "step_bytes_without_crc_reads": put_bytes + fetch_bytes,
         },
+        "step_gbps_without_crc_reads": round((put_bytes + fetch_bytes) / (ms_per_step * 1e-3) / 1e9, 2),
         "roofline": {
             "kernel": "fetch_kernel<fp8,bf16,half_split> (one layer per launch)",
             "bound": "hbm",

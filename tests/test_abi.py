@@ -25,6 +25,34 @@ def test_exports_every_declared_symbol():
         assert getattr(lib, n) is not None
 
 
+def test_header_is_plain_c(tmp_path):
+    """include/hkv.h compiles as C99 with every warning an error, and a C
+    program that takes the address of every declared function links against
+    libhkv.so and runs a host-only call."""
+    import os
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None or not os.path.isdir("/opt/rocm/include"):
+        pytest.skip("needs gcc and the ROCm headers")
+    names = H.declared_symbols()
+    src = tmp_path / "uses_hkv.c"
+    src.write_text('#include "hkv.h"\n'
+                   "int main(void) {\n"
+                   + "".join(f"  (void)&{n};\n" for n in names)
+                   + "  return hkv_record_bytes(HKV_FP8_E4M3, 64, 8, HKV_HEAD_DIM) == 133120 &&\n"
+                     "         hkv_status_string(HKV_ERR_UNSUPPORTED) != 0 ? 0 : 1;\n}\n")
+    pkg = os.path.dirname(H.LIB_PATH)
+    include = os.path.join(os.path.dirname(pkg), "include")
+    exe = tmp_path / "uses_hkv"
+    r = subprocess.run([gcc, "-std=c99", "-Wall", "-Wextra", "-Werror", "-D__HIP_PLATFORM_AMD__",
+                        "-I", "/opt/rocm/include", "-I", include, str(src), "-o", str(exe),
+                        "-L", pkg, "-lhkv", f"-Wl,-rpath,{pkg}"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stderr
+    assert subprocess.run([str(exe)], timeout=60).returncode == 0
+
+
 def test_record_bytes():
     assert H.record_bytes("fp8", 64, 8) == 133120
     assert H.record_bytes("int4", 64, 8) == 67584

@@ -468,6 +468,36 @@ def test_per_token_random_and_extreme_deltas(fmt, tb, H):
             check_keys(kg[:, page], kr[:, b], kd[:, b], "f32", f"K block {b} {pairs}")
 
 
+@pytest.mark.parametrize("fmt", ["fp8", "int4"])
+@pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
+def test_per_block_extreme_deltas(fmt, out_dtype):
+    """Per-block deltas at the ends of the int32 range (phi up to 2^31 rad,
+    the double-precision sincos with full range reduction), 2^30, +-1 and
+    0, both pair conventions."""
+    rng = np.random.default_rng(97)
+    L, P, tb, H = 2, 8, 16, 8
+    kp = rng.standard_normal((L, P, tb, H, 128)).astype(np.float32)
+    vp = rng.standard_normal((L, P, tb, H, 128)).astype(np.float32)
+    table = rng.permutation(P).astype(np.int32)
+    rec, ref, _ = _put_both(kp, vp, table, fmt, "f32")
+    dm = np.array([2 ** 31 - 1, -(2 ** 31), 1 << 30, -1, 1, 0, 7168, -16384], dtype=np.int64)
+    dm = dm.astype(np.int32)
+    ftab = rng.permutation(P).astype(np.int32)
+    tdt = TORCH_OF[out_dtype]
+    for base, pairs in ((1e4, "interleaved"), (5e5, "half_split")):
+        print(f"[small] extreme per-block deltas {fmt} {out_dtype} {pairs}", flush=True)
+        ko = canary_fill(torch.empty((L, P, tb, H, 128), dtype=tdt, device=DEV))
+        vo = canary_fill(torch.empty_like(ko))
+        hkv.fetch_dequant_rope_shift(rec, fmt, _dev_i32(ftab), _dev_i32(dm), base, pairs, ko, vo)
+        torch.cuda.synchronize()
+        kr, vd = O.fetch_exact(ref, fmt, tb, H, dm, base, pairs)
+        kd, _ = O.dequant_records(ref, fmt, tb, H)
+        kg, vg = host_f64(ko), host_f64(vo)
+        for b, page in enumerate(ftab):
+            compare_fetch_block(kg[:, page], vg[:, page], kr[:, b], vd[:, b], kd[:, b],
+                                out_dtype, int(dm[b]), f"block {b} dm={dm[b]} {pairs}")
+
+
 def test_cu_partitioned_stream_pair():
     """A fetch on each stream of hkv_stream_pair_create gives the same pages
     as on the default stream."""

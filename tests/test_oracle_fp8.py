@@ -1,11 +1,22 @@
 """Pins of the oracle's E4M3FN decoder and encoder: the format definition's
 landmarks, torch's CPU float8_e4m3fn conversion, every rounding midpoint and
-the exact round trip of representable values."""
+the exact round trip of representable values.  Two exhaustive sweeps close
+the loop through the threshold fixture, which equals the closed-form midpoint
+rule: torch's conversion of every finite fp32 value (clamped to +-448), and
+the oracle's encoder on every fp32 pattern from 0 to 448."""
+import multiprocessing
+import os
+from concurrent.futures import ProcessPoolExecutor
+
 import numpy as np
 import torch
 
 import oracle as O
 from conftest import load_golden
+from fp8_sweep import expected_steps, observed_steps, oracle_chunk_ok
+
+BITS_448 = 0x43E00000          # fp32 pattern of 448.0, the largest finite E4M3FN value
+BITS_INF = 0x7F800000          # first non-finite positive pattern
 
 
 def _torch_decode(codes):
@@ -97,3 +108,36 @@ def test_encoder_monotone_in_positive_bit_pattern():
     assert np.all(np.diff(c) >= 0)
     th = np.array(load_golden("fp8_thresholds.json")["first_bits_above_code"], dtype=np.int64)
     assert np.array_equal(c, np.searchsorted(th, bits, side="right"))
+
+
+def test_torch_cast_matches_fixture_on_every_finite_value():
+    """Every finite fp32 value, both signs: torch's float8_e4m3fn conversion of
+    the value clamped to +-448 is the fixture's code of |x|, with the sign bit
+    for negative x (including -0)."""
+    th = np.array(load_golden("fp8_thresholds.json")["first_bits_above_code"], dtype=np.int64)
+    chunk = 1 << 24
+    for start in range(0, BITS_INF, chunk):
+        end = min(start + chunk, BITS_INF)
+        x = np.arange(start, end, dtype=np.int64).astype(np.uint32).view(np.float32)
+        np.clip(x, 0.0, 448.0, out=x)
+        pos = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        got_first, got_steps = observed_steps(pos, start)
+        want_first, want_steps = expected_steps(th, start, end)
+        assert got_first == want_first and np.array_equal(got_steps, want_steps), \
+            f"torch and the fixture differ in [{start:#x}, {end:#x})"
+        np.negative(x, out=x)
+        neg = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        assert np.array_equal(neg, pos | 0x80), f"sign handling differs in [{start:#x}, {end:#x})"
+
+
+def test_oracle_encoder_matches_fixture_on_every_pattern_up_to_448():
+    """The oracle's encoder on all 1,138,753,537 fp32 patterns from +0 to 448
+    against the fixture, in chunks over a pool of worker processes."""
+    th = load_golden("fp8_thresholds.json")["first_bits_above_code"]
+    chunk = 1 << 22
+    jobs = [(s, min(s + chunk, BITS_448 + 1), th) for s in range(0, BITS_448 + 1, chunk)]
+    workers = max(1, min(8, len(os.sched_getaffinity(0))))
+    ctx = multiprocessing.get_context("spawn")
+    with ProcessPoolExecutor(max_workers=workers, mp_context=ctx) as ex:
+        bad = [j[:2] for j, ok in zip(jobs, ex.map(oracle_chunk_ok, jobs)) if not ok]
+    assert not bad, f"oracle and fixture differ in chunks {bad[:3]}"

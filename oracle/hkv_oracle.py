@@ -330,10 +330,12 @@ def put(k_pages, v_pages, block_table, fmt):
     rb = record_bytes(fmt, T_b, H, d)
     out = np.zeros((L, nb, rb), dtype=np.uint8)
     live = (table >= 0) & (table < P)
+    if not live.any():
+        return out, live                     # every block skipped: nothing written
     pages = table[live]
     quant = quant_fp8_vectors if fmt == FMT_FP8 else quant_int4_vectors
-    kx = np.asarray(k_pages)[:, pages].astype(np.float32)
-    vx = np.asarray(v_pages)[:, pages].astype(np.float32)
+    kx = np.ascontiguousarray(np.asarray(k_pages)[:, pages], dtype=np.float32)
+    vx = np.ascontiguousarray(np.asarray(v_pages)[:, pages], dtype=np.float32)
     kc, ks = quant(kx)
     vc, vs = quant(vx)
     out[:, live] = assemble_records(kc, vc, ks, vs)

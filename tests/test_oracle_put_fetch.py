@@ -113,3 +113,27 @@ def test_per_token_deltas():
     k_pre, _ = W.tiny_pre_rope_kv()
     rel = np.linalg.norm(kr[0].reshape(64, 8, 128) - k_pre) / np.linalg.norm(k_pre)
     assert rel < 0.05
+
+
+def test_put_with_every_block_skipped_writes_nothing():
+    """A table whose entries are all negative or past the page count: all
+    records stay zero and no block is live."""
+    rng = np.random.default_rng(17)
+    kp = rng.standard_normal((2, 3, 4, 2, 128)).astype(np.float32)
+    for fmt in ("fp8", "int4"):
+        rec, live = O.put(kp, kp, np.array([-1, 3, 7], dtype=np.int32), fmt)
+        assert not live.any() and not rec.any()
+        assert rec.shape == (2, 3, O.record_bytes(fmt, 4, 2))
+
+
+def test_put_is_independent_of_the_input_layout():
+    """Pages given as a strided view (head-major storage seen token-major)
+    give the same records as their contiguous copy."""
+    rng = np.random.default_rng(19)
+    store = rng.standard_normal((2, 4, 3, 5, 128)).astype(np.float32)   # [L, P, H, T_b, d]
+    view = store.transpose(0, 1, 3, 2, 4)                                # [L, P, T_b, H, d]
+    table = np.array([2, 0, -1, 3], dtype=np.int32)
+    for fmt in ("fp8", "int4"):
+        a, la = O.put(view, view * 2, table, fmt)
+        b, lb = O.put(np.ascontiguousarray(view), np.ascontiguousarray(view * 2), table, fmt)
+        assert np.array_equal(a, b) and np.array_equal(la, lb)

@@ -269,6 +269,8 @@ def main():
     ceiling = stream_ceiling(dev, hkv, fetch_launch_bytes, fetch_gbps)
     separate = separate_put_crc(dev, hkv, L, nb, tb, H, src_k, src_v, put_tab, records, crc,
                                 put_bytes, crc_bytes)
+    put_ceiling = put_stream_ceiling(dev, hkv, separate["put"]["gbps"],
+                                     put_bytes / (float(np.mean(put_crc_ms)) * 1e-3) / 1e9)
     frames = frames_leg(dev, hkv, W, w, L, src_k, src_v, put_tab)
     select = recompute_select(dev, hkv, W)
     others = other_workloads(dev, hkv, W)
@@ -334,6 +336,7 @@ def main():
             "ms_80_layers": round(float(np.mean(fetch_span_ms)), 4),
         },
         "ceiling": ceiling,
+        "put_ceiling": put_ceiling,
         "fetch_per_token_delta": {
             "gbps": round(fetch_bytes / (tok_ms * 1e-3) / 1e9, 1),
             "ms_80_layers": round(tok_ms, 4),
@@ -387,6 +390,37 @@ def stream_ceiling(dev, hkv, fetch_launch_bytes, fetch_gbps, nbuf=16, reps=64):
             "gbps": round(gbps, 1),
             "us_per_launch": round(ms * 1e3, 2),
             "fetch_frac_of_ceiling": round(fetch_gbps / gbps, 4)}
+
+
+def put_stream_ceiling(dev, hkv, put_gbps, put_crc_put_gbps, nbuf=16, reps=64):
+    """The put's byte mix with nothing else to do: hkv_stream_probe_put reads
+    272 MB and writes 136 MB per launch (two source bytes per record byte)
+    with the put's load and store pattern, rotating over 16 buffer pairs.
+    HIP events on the current stream.  The put alone and the fused put + CRC
+    pass (counted in put bytes only) are reported as fractions of it."""
+    import torch
+    n_write = 1040 * 1024 * 128
+    src = [torch.full((2 * n_write,), 7, dtype=torch.uint8, device=dev) for _ in range(nbuf)]
+    dst = [torch.empty(n_write, dtype=torch.uint8, device=dev) for _ in range(nbuf)]
+    s = torch.cuda.current_stream(dev)
+    for i in range(2 * nbuf):
+        hkv.stream_probe_put(src[i % nbuf], dst[i % nbuf], stream=s)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record(s)
+    for i in range(reps):
+        hkv.stream_probe_put(src[i % nbuf], dst[i % nbuf], stream=s)
+    ev[1].record(s)
+    s.synchronize()
+    ms = ev[0].elapsed_time(ev[1]) / reps
+    gbps = 3 * n_write / (ms * 1e-3) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"kernel": "hkv_stream_probe_put: 2 bytes read for 1 written, 272 MB read per launch, "
+                      "the put's load and non-temporal store pattern",
+            "gbps": round(gbps, 1),
+            "us_per_launch": round(ms * 1e3, 2),
+            "put_frac_of_ceiling": round(put_gbps / gbps, 4),
+            "put_crc_frac_of_ceiling": round(put_crc_put_gbps / gbps, 4)}
 
 
 def separate_put_crc(dev, hkv, L, nb, tb, H, src_k, src_v, put_tab, records, crc, put_bytes,

@@ -341,6 +341,20 @@ int64_t hkv_select_workspace_bytes(int32_t n_tokens);
  * a multiple of 128; src, dst: device, 16-byte aligned, not overlapping. */
 int hkv_stream_probe(const void* src, void* dst, int64_t bytes_read, hipStream_t stream);
 
+/* Measurement aid, not a step of the method: a plain streaming kernel with
+ * the put's byte mix.  Reads 2 * bytes_written bytes of src and writes
+ * bytes_written bytes to dst: every 256-byte row of src becomes one 128-byte
+ * row of dst, eight threads per row, each loading 16 bytes at offsets 16s and
+ * 128 + 16s of the source row and storing two 8-byte words (xor mixes of
+ * what it loaded) at offsets 8s and 64 + 8s of the output row, non-temporal,
+ * like the put's loads of one bf16 vector and stores of its FP8 codes.
+ * Output word pair of thread s in row r, with x, y the two loaded 16-byte
+ * values as four 32-bit words each: dst[r][8s..] = {x0^y1, x2^y3},
+ * dst[r][64+8s..] = {x1^y0, x3^y2}.  bytes_written: a multiple of 128, at most
+ * 128 * (2^31 - 1) / 8 (HKV_ERR_UNSUPPORTED beyond); src, dst: device,
+ * 16-byte aligned, not overlapping. */
+int hkv_stream_probe_put(const void* src, void* dst, int64_t bytes_written, hipStream_t stream);
+
 /* Host-only helpers. */
 
 /* Bytes of one record: 2*N*C + 4*N (see hkv_records); -1 on bad arguments. */

@@ -346,6 +346,14 @@ int hkv_stream_probe(const void* src, void* dst, int64_t bytes_read, hipStream_t
   return to_status(hkv::launch_stream_expand(src, dst, bytes_read / 16, stream));
 }
 
+int hkv_stream_probe_put(const void* src, void* dst, int64_t bytes_written, hipStream_t stream) {
+  if (bytes_written < 0 || bytes_written % 128 != 0) return HKV_ERR_INVALID_ARG;
+  if (bytes_written / 128 > INT32_MAX / 8) return HKV_ERR_UNSUPPORTED;   // grid of rows * 8 threads
+  if (bytes_written == 0) return HKV_OK;
+  if (!src || !dst || !aligned16(src) || !aligned16(dst)) return HKV_ERR_INVALID_ARG;
+  return to_status(hkv::launch_stream_squeeze(src, dst, bytes_written / 128, stream));
+}
+
 int64_t hkv_select_workspace_bytes(int32_t n_tokens) {
   if (n_tokens < 0 || n_tokens > kMaxSelectTokens) return -1;
   return hkv::select_workspace_bytes(n_tokens);

@@ -59,6 +59,9 @@ hipError_t launch_crc32_merge(const Geometry& g, int64_t record_bytes, const Rec
 // Measurement aid: read units16 x 16 bytes, write each twice (1:2 stream).
 hipError_t launch_stream_expand(const void* src, void* dst, int64_t units16, hipStream_t stream);
 
+// Measurement aid: rows of 256 source bytes -> rows of 128 bytes (2:1 stream).
+hipError_t launch_stream_squeeze(const void* src, void* dst, int64_t rows, hipStream_t stream);
+
 // Frames: a kFrameHeaderBytes header, then the record.
 constexpr int64_t kFrameHeaderBytes = 64;
 

@@ -106,6 +106,8 @@ def lib():
         l.hkv_frame_delta_m.argtypes = [P(Shape), ctypes.c_int32, P(Records), vp, vp, vp]
         l.hkv_stream_probe.argtypes = [vp, vp, ctypes.c_int64, vp]
         l.hkv_stream_probe.restype = ctypes.c_int
+        l.hkv_stream_probe_put.argtypes = [vp, vp, ctypes.c_int64, vp]
+        l.hkv_stream_probe_put.restype = ctypes.c_int
         l.hkv_stream_pair_create.argtypes = [ctypes.c_int32, P(vp), P(vp)]
         l.hkv_stream_pair_create.restype = ctypes.c_int
         l.hkv_stream_destroy.argtypes = [vp]
@@ -517,5 +519,19 @@ def stream_probe(src, dst, stream=None):
         raise ValueError("dst must be contiguous and hold twice src")
     _check("hkv_stream_probe", lib().hkv_stream_probe(
         ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(dst.data_ptr()), src.numel(),
+        _stream(stream, src.device)))
+    return dst
+
+
+@_on_one_gpu
+def stream_probe_put(src, dst, stream=None):
+    """Measurement aid: read src (uint8, twice the size of dst) and write dst
+    (a multiple of 128 bytes) with the put's load and store pattern."""
+    if src.dtype != torch.uint8 or dst.dtype != torch.uint8:
+        raise ValueError("src and dst must be uint8 tensors")
+    if not src.is_contiguous() or not dst.is_contiguous() or src.numel() < 2 * dst.numel():
+        raise ValueError("src must be contiguous and hold twice dst")
+    _check("hkv_stream_probe_put", lib().hkv_stream_probe_put(
+        ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(dst.data_ptr()), dst.numel(),
         _stream(stream, src.device)))
     return dst

@@ -19,7 +19,8 @@ def test_exports_every_declared_symbol():
                           "hkv_select_top_tokens", "hkv_frame_headers", "hkv_frame_verify",
                           "hkv_frame_delta_m", "hkv_select_workspace_bytes",
                           "hkv_quant_fp8_crc", "hkv_quant_int4_crc",
-                          "hkv_quant_crc_workspace_bytes", "hkv_stream_probe"}
+                          "hkv_quant_crc_workspace_bytes", "hkv_stream_probe",
+                          "hkv_stream_probe_put"}
     lib = H.lib()
     for n in names:
         assert getattr(lib, n) is not None
@@ -363,6 +364,19 @@ def test_stream_probe_rejects_bad_arguments():
     assert call(n=-128) == H.ERR_INVALID_ARG
     assert call(src=0) == H.ERR_INVALID_ARG
     assert call(dst=FAKE + 8) == H.ERR_INVALID_ARG
+    assert call(n=0, src=0, dst=0) == H.OK
+
+
+def test_stream_probe_put_rejects_bad_arguments():
+    lib = H.lib()
+    call = lambda src=FAKE, dst=FAKE + (1 << 20), n=1024: lib.hkv_stream_probe_put(
+        ctypes.c_void_p(src), ctypes.c_void_p(dst), n, None)
+    assert call(n=1000) == H.ERR_INVALID_ARG          # not a multiple of 128
+    assert call(n=-128) == H.ERR_INVALID_ARG
+    assert call(src=0) == H.ERR_INVALID_ARG
+    assert call(src=FAKE + 8) == H.ERR_INVALID_ARG
+    assert call(dst=FAKE + 8) == H.ERR_INVALID_ARG
+    assert call(n=128 * ((1 << 28) + 1)) == H.ERR_UNSUPPORTED   # more rows than the grid holds
     assert call(n=0, src=0, dst=0) == H.OK
 
 

@@ -289,6 +289,25 @@ def test_stream_probe_pattern():
     assert np.array_equal(d16[o], s16) and np.array_equal(d16[o + 8], s16 ^ np.uint32(0x5A5A5A5A))
 
 
+def test_stream_probe_put_pattern():
+    """The put-mix measurement aid: row r of the output holds, for s in 0..7,
+    the words {x0^y1, x2^y3} at 8s and {x1^y0, x3^y2} at 64 + 8s, where x and
+    y are the 16-byte words at 16s and 128 + 16s of source row r."""
+    rng = np.random.default_rng(79)
+    rows = 1000
+    src_np = rng.integers(0, 256, 256 * rows, dtype=np.uint8)
+    src = torch.from_numpy(src_np).to(DEV)
+    dst = torch.zeros(128 * rows, dtype=torch.uint8, device=DEV)
+    hkv.stream_probe_put(src, dst)
+    torch.cuda.synchronize()
+    w = src_np.view(np.uint32).reshape(rows, 2, 8, 4)      # [row, half, s, word]
+    x, y = w[:, 0], w[:, 1]
+    lo = np.stack([x[..., 0] ^ y[..., 1], x[..., 2] ^ y[..., 3]], axis=-1)   # [row, s, 2]
+    hi = np.stack([x[..., 1] ^ y[..., 0], x[..., 3] ^ y[..., 2]], axis=-1)
+    want = np.concatenate([lo.reshape(rows, 16), hi.reshape(rows, 16)], axis=1)
+    assert np.array_equal(dst.cpu().numpy().view(np.uint32).reshape(rows, 32), want)
+
+
 def test_scale_edge_cases_fp32_source():
     """All-zero vectors (with signed zeros), scales that underflow or
     overflow fp16, and saturation beyond 448."""

@@ -14,10 +14,16 @@
 // Work decomposition: one workgroup (4 waves) per (layer, block, K|V, chunk
 // of 4 * PASSES * 8 vectors), PASSES * 8 consecutive vectors per wave, 8
 // lanes per vector; the vector's amax is reduced over its 8 lanes with
-// cross-lane max.  PASSES is 4 when a block's vector count is a multiple of
-// 128 (chunks of 128), else 2 (chunks of 64).  Measured on MI355X: the
-// INT4 put 7% faster with four passes; the FP8 put from bf16, fused or not,
-// 4% faster on 8 layers and unchanged on 80; the FP8 put from fp16 unchanged.
+// cross-lane max.  Passes per wave, measured on MI355X (one launch over all
+// layers, permuted tables):
+// * the FP8 put from fp16 or bf16 makes one pass (chunks of 32 vectors): 2-3.5%
+//   faster than four passes at the Llama-3-70B and Qwen3-8B shapes;
+// * the INT4 put makes four (chunks of 128) when the block's vector count is a
+//   multiple of 128, else two: one pass is 10-20% slower, two 5% slower;
+// * the fused put + CRC makes four (or two) as well: its per-workgroup CRC
+//   setup (byte tables, a barrier) would run four times as often with one
+//   pass, 10% slower;
+// * the FP8 put from fp32 sources (small workloads only) keeps four or two.
 #include "crc_device.h"
 #include "hkv_device.h"
 #include "hkv_launch.h"
@@ -277,7 +283,7 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(QuantParams p) {
 template <int FMT, int SDT, bool CRC, int PASSES>
 hipError_t launch_passes(QuantParams p, const Geometry& g, hipStream_t stream) {
   p.vecs_per_chunk = kVecsPerWave * PASSES * (kThreads / kWave);
-  static_assert(kVecsPerWave * 2 * (kThreads / kWave) >= kFetchMinGroupVecs,
+  static_assert(kVecsPerWave * PASSES * (kThreads / kWave) >= kFetchMinGroupVecs,
                 "the shape check bounds the chunk count with the smallest chunk");
   p.chunks = (g.vecs + p.vecs_per_chunk - 1) / p.vecs_per_chunk;
   dim3 grid(static_cast<unsigned>(g.n_blocks) * 2u * static_cast<unsigned>(p.chunks),
@@ -286,10 +292,12 @@ hipError_t launch_passes(QuantParams p, const Geometry& g, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// Four passes when the block's vectors fill chunks of 128, else two (the
-// fused path requires whole chunks: vecs % 64 == 0, checked by the caller).
+// One pass for the FP8 put from 16-bit sources; otherwise four passes when
+// the block's vectors fill chunks of 128, else two (the fused path requires
+// whole chunks: vecs % 64 == 0, checked by the caller).
 template <int FMT, int SDT, bool CRC>
 hipError_t launch_t(const QuantParams& p, const Geometry& g, hipStream_t stream) {
+  if constexpr (FMT == kFP8 && SDT != kF32 && !CRC) return launch_passes<FMT, SDT, CRC, 1>(p, g, stream);
   return g.vecs % 128 == 0 ? launch_passes<FMT, SDT, CRC, 4>(p, g, stream)
                            : launch_passes<FMT, SDT, CRC, 2>(p, g, stream);
 }

@@ -454,9 +454,10 @@ def separate_put_crc(dev, hkv, L, nb, tb, H, src_k, src_v, put_tab, records, crc
 
 
 def other_workloads(dev, hkv, W, reps=5):
-    """Put and fetch throughput on the Qwen3-8B-shaped (FP8, fp16 pages, random
-    per-block deltas) and INT4 disk-tier (fp16 with outlier channels) caches,
-    all layers in one call per operation.  Outside the step; HIP events."""
+    """Put, put + CRC-32 in one pass, and fetch throughput on the Qwen3-8B-shaped
+    (FP8, fp16 pages, random per-block deltas) and INT4 disk-tier (fp16 with
+    outlier channels) caches, all layers in one call per operation.  Outside
+    the step; HIP events."""
     import numpy as np
     import torch
     res = {}
@@ -494,6 +495,20 @@ def other_workloads(dev, hkv, W, reps=5):
             if rep:
                 put_ms.append(ev[0].elapsed_time(ev[1]))
                 fetch_ms.append(ev[1].elapsed_time(ev[2]))
+        # the put with the CRC-32 of every record in one pass (the disk tier
+        # writes its records with their CRCs)
+        crc = torch.empty((L, nb), dtype=torch.int32, device=dev)
+        ws = torch.empty(max(16, hkv.quant_crc_workspace_bytes(fmt, L, nb, tb, H)),
+                         dtype=torch.uint8, device=dev)
+        put_crc_ms = []
+        for rep in range(reps + 1):
+            ev[0].record(s)
+            hkv.quant_crc(fmt, src_k, src_v, put_tab, rec, crc_out=crc, workspace=ws, stream=s)
+            ev[1].record(s)
+            s.synchronize()
+            if rep:
+                put_crc_ms.append(ev[0].elapsed_time(ev[1]))
+        del crc, ws
         cb = 128 if fmt == "fp8" else 64
         vecs = 2 * L * w.n_tokens * H
         es = src_k.element_size()
@@ -508,6 +523,9 @@ def other_workloads(dev, hkv, W, reps=5):
             "fetch_tokens_per_s": round(w.n_tokens / (fms * 1e-3), 0),
             "put_ms": round(pms, 4),
             "put_gbps": round(put_bytes / (pms * 1e-3) / 1e9, 1),
+            "put_crc_ms": round(float(np.mean(put_crc_ms)), 4),
+            "put_crc_gbps_put_bytes": round(put_bytes / (float(np.mean(put_crc_ms)) * 1e-3) / 1e9,
+                                            1),
         }
         del src_k, src_v, rec, out_k, out_v
         torch.cuda.empty_cache()

@@ -149,8 +149,7 @@ int hkv_quant_int4(const hkv_shape* shape, const hkv_pages* src, int32_t src_dty
  * hkv_quant_fp8 / hkv_quant_int4 and to crc_out (uint32 [n_layers *
  * n_blocks], device, layer-major) the CRC-32 of every record the put wrote,
  * equal to what hkv_crc32_blocks computes over them.  Entries of skipped
- * blocks are left unchanged by the one-pass path; the two-pass fallback
- * (below) writes the CRC of whatever those records hold.  The put kernel
+ * blocks are left unchanged (on both paths below).  The put kernel
  * stages each workgroup's codes in LDS and stores the raw CRC of every
  * 128-byte unit of the record's codes to `workspace`; a second kernel reads
  * each record's scales back and merges both into the record's CRC.  The
@@ -217,7 +216,8 @@ int hkv_fetch_dequant_rope_shift_tokens(const hkv_shape* shape, int32_t fmt,
  * block_table[b]; blocks whose entry is negative or >= num_pages come last,
  * in index order (ties, which the fetch contract excludes, by index).  This
  * is a scheduling aid, not a step of the method; O(n_blocks^2) work, meant
- * for tables of up to a few thousand blocks. */
+ * for tables of up to a few thousand blocks; n_blocks above 65,536 returns
+ * HKV_ERR_UNSUPPORTED. */
 int hkv_page_visit_order(const int32_t* block_table, int32_t n_blocks, int32_t num_pages,
                          int32_t* order_out, hipStream_t stream);
 

@@ -73,5 +73,22 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+def build_test_kernels(verbose: bool = False) -> list:
+    """Test-only HIP libraries under tests/hip/ (each built from one source
+    with the library's flags and device headers); the GPU tests load them."""
+    cc = hipcc()
+    out = []
+    tests_hip = os.path.join(ROOT, "tests", "hip")
+    for src in sorted(os.listdir(tests_hip)):
+        if not src.endswith(".hip"):
+            continue
+        lib = os.path.join(tests_hip, "lib" + os.path.splitext(src)[0] + ".so")
+        _run([cc, *compile_flags(), "-shared", os.path.join(tests_hip, src), "-o", lib + ".tmp"],
+             verbose)
+        os.replace(lib + ".tmp", lib)
+        out.append(lib)
+    return out
+
+
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))

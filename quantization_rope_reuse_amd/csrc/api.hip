@@ -91,6 +91,8 @@ int check_records(const hkv_records* r, int32_t fmt, const hkv_shape* s, RecordV
 int to_status(hipError_t e) { return e == hipSuccess ? HKV_OK : HKV_ERR_HIP; }
 
 constexpr int32_t kMaxSelectTokens = 1 << 30;
+// hkv_page_visit_order compares every pair of blocks (n^2 / 64 wave steps).
+constexpr int32_t kMaxOrderBlocks = 1 << 16;
 
 // Frames: the records view describes the frames; each frame must hold the
 // header and the record.  Fills the launch geometry and the frame view.
@@ -134,6 +136,23 @@ int64_t quant_crc_workspace(const Geometry& g, int64_t rb) {
   return static_cast<int64_t>(g.n_layers) * g.n_blocks * (rb / 128) * 4;
 }
 
+// Argument checks of the fused put + CRC, everything but the workspace.
+int quant_crc_check(int32_t fmt, const hkv_shape* shape, const hkv_pages* src,
+                    int32_t src_dtype, const int32_t* block_table, const hkv_records* dst,
+                    const uint32_t* crc_out, Geometry* g, PageView* pv, RecordView* rv,
+                    int64_t* rb, int64_t* need) {
+  int st;
+  if ((st = check_shape(shape, g)) != HKV_OK) return st;
+  if ((st = check_pages(src, src_dtype, pv)) != HKV_OK) return st;
+  if ((st = check_records(dst, fmt, shape, rv)) != HKV_OK) return st;
+  if (!block_table && g->n_blocks > 0) return HKV_ERR_INVALID_ARG;
+  if (!crc_out && g->n_layers > 0 && g->n_blocks > 0) return HKV_ERR_INVALID_ARG;
+  *rb = hkv_record_bytes(fmt, shape->block_tokens, shape->n_kv_heads, shape->head_dim);
+  if (*rb > (int64_t{1} << 30)) return HKV_ERR_UNSUPPORTED;
+  *need = quant_crc_workspace(*g, *rb);
+  return HKV_OK;
+}
+
 int quant_crc_common(int32_t fmt, const hkv_shape* shape, const hkv_pages* src,
                      int32_t src_dtype, const int32_t* block_table, const hkv_records* dst,
                      uint32_t* crc_out, void* workspace, int64_t workspace_bytes,
@@ -141,23 +160,18 @@ int quant_crc_common(int32_t fmt, const hkv_shape* shape, const hkv_pages* src,
   Geometry g;
   PageView pv;
   RecordView rv;
-  int st;
-  if ((st = check_shape(shape, &g)) != HKV_OK) return st;
-  if ((st = check_pages(src, src_dtype, &pv)) != HKV_OK) return st;
-  if ((st = check_records(dst, fmt, shape, &rv)) != HKV_OK) return st;
-  if (!block_table && g.n_blocks > 0) return HKV_ERR_INVALID_ARG;
-  if (!crc_out && g.n_layers > 0 && g.n_blocks > 0) return HKV_ERR_INVALID_ARG;
-  const int64_t rb = hkv_record_bytes(fmt, shape->block_tokens, shape->n_kv_heads,
-                                      shape->head_dim);
-  if (rb > (int64_t{1} << 30)) return HKV_ERR_UNSUPPORTED;
-  const int64_t need = quant_crc_workspace(g, rb);
+  int64_t rb, need;
+  const int st = quant_crc_check(fmt, shape, src, src_dtype, block_table, dst, crc_out, &g, &pv,
+                                 &rv, &rb, &need);
+  if (st != HKV_OK) return st;
   if (need > 0 && (!workspace || !aligned16(workspace) || workspace_bytes < need))
     return HKV_ERR_INVALID_ARG;
   if (g.n_layers == 0 || g.n_blocks == 0) return HKV_OK;
   if (need == 0) {
     const hipError_t e = hkv::launch_quant(fmt, src_dtype, g, pv, block_table, rv, stream);
     if (e != hipSuccess) return HKV_ERR_HIP;
-    return to_status(hkv::launch_crc32(g, rb, rv, crc_out, stream));
+    // the CRCs of skipped blocks stay unchanged, as on the one-pass path
+    return to_status(hkv::launch_crc32(g, rb, rv, block_table, pv.num_pages, crc_out, stream));
   }
   uint32_t* partials = static_cast<uint32_t*>(workspace);
   const hipError_t e = hkv::launch_quant_crc_units(fmt, src_dtype, g, pv, block_table, rv, rb,
@@ -264,6 +278,7 @@ int hkv_fetch_dequant_rope_shift_tokens(const hkv_shape* shape, int32_t fmt,
 int hkv_page_visit_order(const int32_t* block_table, int32_t n_blocks, int32_t num_pages,
                          int32_t* order_out, hipStream_t stream) {
   if (n_blocks < 0 || num_pages < 0) return HKV_ERR_INVALID_ARG;
+  if (n_blocks > kMaxOrderBlocks) return HKV_ERR_UNSUPPORTED;
   if (n_blocks == 0) return HKV_OK;
   if (!block_table || !order_out) return HKV_ERR_INVALID_ARG;
   return to_status(hkv::launch_page_order(block_table, n_blocks, num_pages, order_out, stream));
@@ -282,7 +297,7 @@ int hkv_crc32_blocks(const hkv_shape* shape, int32_t fmt, const hkv_records* src
   const int64_t rb = hkv_record_bytes(fmt, shape->block_tokens, shape->n_kv_heads,
                                       shape->head_dim);
   if (rb > (int64_t{1} << 30)) return HKV_ERR_UNSUPPORTED;
-  return to_status(hkv::launch_crc32(g, rb, rv, crc_out, stream));
+  return to_status(hkv::launch_crc32(g, rb, rv, nullptr, 0, crc_out, stream));
 }
 
 int hkv_frame_headers(const hkv_shape* shape, int32_t fmt, const hkv_records* frames,

@@ -31,6 +31,8 @@ struct CrcParams {
   const uint8_t* rec;
   int64_t rec_layer, rec_block;
   uint32_t* out;
+  const int32_t* table;  // optional: skip the records of skipped blocks
+  int32_t num_pages;
   int32_t n_blocks;
   int32_t n_records;
   int32_t chunk;         // bytes per lane (multiple of 4)
@@ -95,6 +97,10 @@ __global__ __launch_bounds__(kThreads) void crc32_kernel(CrcParams p) {
   if (r >= p.n_records) return;                 // whole wave, after the barriers
   const int layer = r / p.n_blocks;
   const int blk = r - layer * p.n_blocks;
+  if (p.table) {
+    const int page = p.table[blk];
+    if (page < 0 || page >= p.num_pages) return;  // whole wave: a skipped block
+  }
   const uint8_t* rec = p.rec + layer * p.rec_layer + blk * p.rec_block;
 
   const int64_t start = static_cast<int64_t>(lane) * p.chunk - p.pad;   // may be < 0
@@ -230,12 +236,15 @@ __global__ __launch_bounds__(kThreads) void crc32_merge_kernel(MergeParams p) {
 }  // namespace
 
 hipError_t launch_crc32(const Geometry& g, int64_t record_bytes, const RecordView& src,
-                        uint32_t* out, hipStream_t stream) {
+                        const int32_t* table, int32_t num_pages, uint32_t* out,
+                        hipStream_t stream) {
   CrcParams p;
   p.rec = src.base;
   p.rec_layer = src.layer;
   p.rec_block = src.block;
   p.out = out;
+  p.table = table;
+  p.num_pages = num_pages;
   p.n_blocks = g.n_blocks;
   p.n_records = g.n_layers * g.n_blocks;
   // Lane chunks are whole 128-byte cache lines when the record size allows

@@ -154,7 +154,7 @@ hipError_t launch_frame_verify(int fmt, const Geometry& g, const RecordView& fra
                                int64_t record_bytes, int32_t layer_base, uint32_t* status,
                                hipStream_t stream) {
   const RecordView payload{frames.base + kFrameHeaderBytes, frames.layer, frames.block};
-  hipError_t e = launch_crc32(g, record_bytes, payload, status, stream);
+  hipError_t e = launch_crc32(g, record_bytes, payload, nullptr, 0, status, stream);
   if (e != hipSuccess) return e;
   const FrameParams p = make_params(fmt, g, frames, record_bytes, layer_base);
   hipLaunchKernelGGL(frame_verify_kernel,

@@ -78,6 +78,22 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float x) {
   return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
 }
 
+// x / s rounded to nearest even in fp32, given r = 1/s rounded to nearest
+// even (one IEEE division per scale): q0 = x*r is within a few ulps of x/s,
+// the remainder x - q0*s is exact in one fused multiply-add, and one
+// correction step q0 + rem*r rounds to the correctly rounded quotient
+// (Markstein's correction on a correctly rounded reciprocal).  A GPU test
+// compares it with IEEE division for every fp32 significand of x against
+// every fp16 significand of s at several exponent pairs (bitwise equal);
+// power-of-two scaling carries that to every quotient whose remainder stays
+// a normal number, which covers every quotient the put turns into a code.
+// The sign is taken from x so that signed zeros agree.
+__device__ __forceinline__ float div_by_scale(float x, float s, float r) {
+  const float q0 = x * r;
+  const float rem = __builtin_fmaf(-q0, s, x);
+  return __builtin_copysignf(__builtin_fmaf(rem, r, q0), x);
+}
+
 // ---------------------------------------------------------------------------
 // 8-element runs: load as fp32 / store from fp32
 // ---------------------------------------------------------------------------

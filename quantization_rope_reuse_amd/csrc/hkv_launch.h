@@ -40,8 +40,11 @@ hipError_t launch_fetch(int fmt, int dst_dtype, int pairs, const Geometry& g,
 hipError_t launch_page_order(const int32_t* table, int32_t n_blocks, int32_t num_pages,
                              int32_t* order, hipStream_t stream);
 
+// table: NULL (every record), or the block table: records of blocks whose
+// entry is negative or >= num_pages are skipped and their CRCs not written.
 hipError_t launch_crc32(const Geometry& g, int64_t record_bytes, const RecordView& src,
-                        uint32_t* out, hipStream_t stream);
+                        const int32_t* table, int32_t num_pages, uint32_t* out,
+                        hipStream_t stream);
 
 // Fused put + CRC: the put also writes the raw CRC of every 128-byte unit of
 // the codes of every record to `partials` (layer-major, record_bytes / 128

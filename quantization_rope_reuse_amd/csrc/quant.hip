@@ -94,21 +94,6 @@ __device__ __forceinline__ void run_to_f32(const RawSrc<SDT>& r, float (&x)[8]) 
   }
 }
 
-// x / s rounded to nearest even in fp32, given r = 1/s rounded to nearest
-// even: q0 = x*r is within a few ulps of x/s, the remainder x - q0*s is exact
-// in one fused multiply-add, and one correction step q0 + rem*r rounds to the
-// correctly rounded quotient (Markstein's theorem on division by a correctly
-// rounded reciprocal).  An exhaustive GPU comparison with IEEE division, every
-// positive fp32 x against every fp16 scale significand, found bitwise equality
-// wherever the quotient is a normal number; where it underflows the two can
-// differ in the last subnormal bit, which no FP8 or INT4 code can see, and the
-// sign is taken from x so that signed zeros agree.
-__device__ __forceinline__ float div_by_scale(float x, float s, float r) {
-  const float q0 = x * r;
-  const float rem = __builtin_fmaf(-q0, s, x);
-  return __builtin_copysignf(__builtin_fmaf(rem, r, q0), x);
-}
-
 // Quantize one vector's lane-owned runs a (elements 8s..8s+7) and b
 // (64+8s..64+8s+7); returns the fp16 scale bits (same in all 8 lanes).
 // STAGE: the code bytes also go to `stage` (LDS) at the same offsets.

@@ -168,10 +168,16 @@ def _pages(k: torch.Tensor, v: torch.Tensor):
     return p, k5.shape, TORCH_DTYPES[k5.dtype]
 
 
-def _records(r: torch.Tensor):
-    """Records as a uint8 tensor [L, n_blocks, >= record_bytes]."""
+def _records(r: torch.Tensor, fmt, block_tokens: int, n_kv_heads: int, header: int = 0):
+    """Records as a uint8 tensor [L, n_blocks, >= header + record_bytes]: the
+    last axis must hold a whole record of this format and shape (and the
+    header, for frames), since the library can only compare strides."""
     if r.dtype != torch.uint8 or r.dim() != 3 or r.stride(2) != 1:
         raise ValueError("records must be a uint8 [L, n_blocks, bytes] tensor, last axis contiguous")
+    need = header + record_bytes(fmt, block_tokens, n_kv_heads)
+    if r.shape[2] < need:
+        raise ValueError(f"records hold {r.shape[2]} bytes per block; a {fmt} record of "
+                         f"{block_tokens} tokens x {n_kv_heads} heads needs {need}")
     return Records(r.data_ptr(), r.stride(0), r.stride(1))
 
 
@@ -218,13 +224,13 @@ def alloc_records(n_layers: int, n_blocks: int, fmt, block_tokens: int, n_kv_hea
 # The four calls
 # ---------------------------------------------------------------------------
 
-def _quant(name, k_pages, v_pages, block_table, records, stream):
+def _quant(name, fmt, k_pages, v_pages, block_table, records, stream):
     pages, shp, dt = _pages(k_pages, v_pages)
     L, _, tb, H, d = shp
     if records.shape[0] != L or records.shape[1] != block_table.numel():
         raise ValueError("records must be [L, n_blocks, bytes] matching pages and table")
     shape = Shape(L, block_table.numel(), tb, H, d)
-    rec = _records(records)
+    rec = _records(records, fmt, tb, H)
     st = getattr(lib(), name)(ctypes.byref(shape), ctypes.byref(pages), dt,
                               _i32(block_table, "block_table"), ctypes.byref(rec),
                               _stream(stream, k_pages.device))
@@ -235,13 +241,13 @@ def _quant(name, k_pages, v_pages, block_table, records, stream):
 @_on_one_gpu
 def quant_fp8(k_pages, v_pages, block_table, records, stream=None):
     """Quantize the blocks k/v_pages[:, block_table[b]] into records[:, b] (FP8)."""
-    return _quant("hkv_quant_fp8", k_pages, v_pages, block_table, records, stream)
+    return _quant("hkv_quant_fp8", "fp8", k_pages, v_pages, block_table, records, stream)
 
 
 @_on_one_gpu
 def quant_int4(k_pages, v_pages, block_table, records, stream=None):
     """Quantize the blocks k/v_pages[:, block_table[b]] into records[:, b] (INT4)."""
-    return _quant("hkv_quant_int4", k_pages, v_pages, block_table, records, stream)
+    return _quant("hkv_quant_int4", "int4", k_pages, v_pages, block_table, records, stream)
 
 
 def quant_crc_workspace_bytes(fmt, n_layers: int, n_blocks: int, block_tokens: int,
@@ -272,7 +278,7 @@ def quant_crc(fmt, k_pages, v_pages, block_table, records, crc_out=None, workspa
     if workspace.dtype != torch.uint8 or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous uint8 tensor")
     shape = Shape(L, nb, tb, H, d)
-    rec = _records(records)
+    rec = _records(records, fmt, tb, H)
     name = "hkv_quant_fp8_crc" if FORMATS[fmt] == FP8_E4M3 else "hkv_quant_int4_crc"
     st = getattr(lib(), name)(ctypes.byref(shape), ctypes.byref(pages), dt,
                               _i32(block_table, "block_table"), ctypes.byref(rec),
@@ -293,7 +299,7 @@ def _fetch(name, records, fmt, block_table, delta, n_delta, rope_base, pairs, k_
     if visit_order is not None and visit_order.numel() != nb:
         raise ValueError("visit_order must hold n_blocks entries")
     shape = Shape(L, nb, tb, H, d)
-    rec = _records(records)
+    rec = _records(records, fmt, tb, H)
     order = None if visit_order is None else _i32(visit_order, "visit_order")
     st = getattr(lib(), name)(
         ctypes.byref(shape), FORMATS[fmt], ctypes.byref(rec), _i32(block_table, "block_table"),
@@ -368,7 +374,7 @@ def crc32_blocks(records, fmt, block_tokens: int, n_kv_heads: int, out=None, str
     if out.dtype != torch.int32 or not out.is_contiguous() or out.numel() != L * nb:
         raise ValueError("out must be a contiguous int32 tensor of L * n_blocks elements")
     shape = Shape(L, nb, block_tokens, n_kv_heads, HEAD_DIM)
-    rec = _records(records)
+    rec = _records(records, fmt, block_tokens, n_kv_heads)
     st = lib().hkv_crc32_blocks(ctypes.byref(shape), FORMATS[fmt], ctypes.byref(rec),
                                 ctypes.c_void_p(out.data_ptr()), _stream(stream, records.device))
     _check("hkv_crc32_blocks", st)
@@ -458,7 +464,7 @@ def _frame_args(frames, fmt, block_tokens, n_kv_heads):
     if frames.dim() != 3:
         raise ValueError("frames must be a uint8 [L, n_blocks, bytes] tensor")
     shape = Shape(frames.shape[0], frames.shape[1], block_tokens, n_kv_heads, HEAD_DIM)
-    return shape, _records(frames)
+    return shape, _records(frames, fmt, block_tokens, n_kv_heads, header=FRAME_HEADER_BYTES)
 
 
 @_on_one_gpu

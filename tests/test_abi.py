@@ -208,6 +208,9 @@ def test_page_order_rejects_bad_arguments():
     assert lib.hkv_page_visit_order(ctypes.c_void_p(FAKE), -1, 4, ctypes.c_void_p(FAKE),
                                     None) == H.ERR_INVALID_ARG
     assert lib.hkv_page_visit_order(None, 0, 4, None, None) == H.OK
+    # the O(n^2) rank kernel takes at most 65,536 blocks
+    assert lib.hkv_page_visit_order(ctypes.c_void_p(FAKE), (1 << 16) + 1, 4,
+                                    ctypes.c_void_p(FAKE), None) == H.ERR_UNSUPPORTED
 
 
 def test_binding_validates_tensors_before_calling():
@@ -354,6 +357,21 @@ def test_fused_put_crc_rejects_bad_arguments():
     assert call(wsb=need - 1) == H.ERR_INVALID_ARG
     assert call(ws=FAKE + 4100) == H.ERR_INVALID_ARG               # misaligned
     assert call(sh=_shape(n_blocks=0), crc=0, ws=0, wsb=0) == H.OK
+
+
+def test_binding_checks_record_size():
+    """A records tensor whose last axis is shorter than one record of the
+    call's format and shape is refused by the binding (the library can only
+    compare strides, and a single record has none)."""
+    import torch
+    int4_rec = torch.zeros((1, 1, H.record_bytes("int4", 16, 8)), dtype=torch.uint8)
+    fp8_rec = torch.zeros((1, 1, H.record_bytes("fp8", 16, 8)), dtype=torch.uint8)
+    with pytest.raises(ValueError, match="needs 33280"):
+        H._records(int4_rec, "fp8", 16, 8)
+    assert H._records(fp8_rec, "fp8", 16, 8).base == fp8_rec.data_ptr()
+    assert H._records(fp8_rec, "int4", 16, 8).block_stride_bytes == fp8_rec.stride(1)
+    with pytest.raises(ValueError, match="needs 33344"):          # a frame: 64 + record
+        H._records(fp8_rec, "fp8", 16, 8, header=64)
 
 
 def test_stream_probe_rejects_bad_arguments():

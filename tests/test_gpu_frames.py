@@ -134,10 +134,10 @@ def test_disk_round_trip_and_tamper(tmp_path):
     assert want[0, 3] & O.FRAME_BAD_MAGIC and want[1, 40] & O.FRAME_BAD_INDEX
     assert np.count_nonzero(want) >= 5
     # a wrong shape or layer base flags every frame; FP8 frames would not fit
-    # this buffer's stride, which the host check rejects before any launch
+    # this buffer, which the binding rejects before any library call
     bad_geo = hkv.frame_verify(back, fmt, w.block_tokens // 2, w.n_kv_heads).cpu().numpy()
     assert (bad_geo & O.FRAME_BAD_GEOMETRY).all()
-    with pytest.raises(hkv.HkvError):
+    with pytest.raises(ValueError, match="needs"):
         hkv.frame_verify(back, "fp8", w.block_tokens, w.n_kv_heads)
     bad_layer = hkv.frame_verify(back, fmt, w.block_tokens, w.n_kv_heads,
                                  layer_base=1).cpu().numpy()

@@ -210,7 +210,7 @@ def test_large_blocks(fmt):
 def test_fused_put_crc(fmt, shape):
     """Put and CRC in one pass: the records equal the separate put's, the CRCs
     equal the oracle's for every written block, and the entries of skipped
-    blocks stay as they were.  Blocks of 128k vectors run the put's four-pass
+    blocks stay as they were (on both paths).  Blocks of 128k vectors run the put's four-pass
     chunks (128 vectors); 24 x 8 = 192 and 8 x 8 = 64 vectors its two-pass
     chunks (64), and give the merge 3 and 1 scale words per lane.  37 x 9 =
     333 vectors per block is not a multiple of 64: that shape runs the put and
@@ -239,7 +239,7 @@ def test_fused_put_crc(fmt, shape):
     for b in range(len(table)):
         if live[b]:
             assert np.array_equal(got[:, b], want[:, b]), f"block {b} CRC"
-        elif tb * H % 64 == 0:
+        else:      # on the one-pass path and on the put-then-CRC path alike
             assert (got[:, b] == 0x1234567).all(), f"skipped block {b} CRC was written"
 
 
@@ -271,6 +271,25 @@ def test_fused_put_crc_other_sources(fmt, src_dtype):
             assert np.array_equal(got[:, b], want[:, b]), f"block {b} CRC"
         else:
             assert (got[:, b] == 0x1234567).all(), f"skipped block {b} CRC was written"
+
+
+def test_binding_refuses_short_records():
+    """A records tensor with too few bytes per block for the call's format
+    (an INT4-sized buffer given to the FP8 put and fetch, a record-sized
+    buffer given as frames) raises before any library call."""
+    tb, H = 16, 8
+    k = torch.zeros((1, 1, tb, H, 128), dtype=torch.bfloat16, device=DEV)
+    tab = torch.zeros(1, dtype=torch.int32, device=DEV)
+    short = hkv.alloc_records(1, 1, "int4", tb, H, device=DEV)
+    with pytest.raises(ValueError, match="needs"):
+        hkv.quant_fp8(k, k, tab, short)
+    with pytest.raises(ValueError, match="needs"):
+        hkv.fetch_dequant_rope_shift(short, "fp8", tab, tab, 1e4, "interleaved", k, k)
+    with pytest.raises(ValueError, match="needs"):
+        hkv.crc32_blocks(short, "fp8", tb, H)
+    rec = hkv.alloc_records(1, 1, "fp8", tb, H, device=DEV)
+    with pytest.raises(ValueError, match="needs"):
+        hkv.frame_verify(rec, "fp8", tb, H)
 
 
 def test_stream_probe_pattern():

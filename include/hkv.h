@@ -41,7 +41,8 @@
  * - Calls are asynchronous on `stream` (0 = the default stream), allocate
  *   no memory (hkv_stream_pair_create aside, which creates two streams),
  *   keep no state between calls and may be called from several host
- *   threads at once.
+ *   threads at once; hkv_quant_fp8_crc_noalloc is the one exception to the
+ *   last two: it works in a scratch array the library keeps per GPU.
  * - Return value: HKV_OK (0) or a negative hkv_status.  Argument errors are
  *   detected on the host before anything is launched; nothing throws across
  *   the ABI.  A launch failure is reported as HKV_ERR_HIP.
@@ -168,6 +169,25 @@ int hkv_quant_int4_crc(const hkv_shape* shape, const hkv_pages* src, int32_t src
 /* Workspace bytes for hkv_quant_*_crc with this shape and format; -1 on bad
  * arguments. */
 int64_t hkv_quant_crc_workspace_bytes(const hkv_shape* shape, int32_t fmt);
+
+/* hkv_quant_fp8_crc for callers that cannot allocate device memory (code
+ * under HIP graph capture, serving loops that never call the allocator,
+ * harnesses that forbid it).  Same arguments, records and CRCs as
+ * hkv_quant_fp8_crc, without the workspace: the call uses a scratch array
+ * of HKV_NOALLOC_SCRATCH_BYTES that the library holds in device memory, one
+ * per GPU it runs on, for the life of the process, and calls no allocator.
+ * A shape whose hkv_quant_crc_workspace_bytes(shape, HKV_FP8_E4M3) exceeds
+ * HKV_NOALLOC_SCRATCH_BYTES (about 1 GiB of records; one Llama-3-70B-shaped
+ * layer needs 4.3 MB) returns HKV_ERR_UNSUPPORTED before anything runs:
+ * split it into several calls.  The scratch belongs to the device of
+ * `stream`; its contents between calls do not matter.  All calls on one GPU
+ * share that GPU's scratch, so calls that overlap in time on one GPU (on
+ * different streams, or from several host threads without ordering) race
+ * and must not be made. */
+#define HKV_NOALLOC_SCRATCH_BYTES (32LL * 1024 * 1024)
+int hkv_quant_fp8_crc_noalloc(const hkv_shape* shape, const hkv_pages* src, int32_t src_dtype,
+                              const int32_t* block_table, const hkv_records* dst,
+                              uint32_t* crc_out, hipStream_t stream);
 
 /* Fetch (HyperCache post: Core Design, relative-RoPE paragraph; Part B, the
  * socket-fetch line with RoPE applied on the fly).

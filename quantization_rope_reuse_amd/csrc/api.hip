@@ -204,6 +204,21 @@ int fetch_common(const hkv_shape* shape, int32_t fmt, const hkv_records* src,
 
 }  // namespace
 
+namespace hkv {
+
+int quant_crc_validate(int32_t fmt, const hkv_shape* shape, const hkv_pages* src,
+                       int32_t src_dtype, const int32_t* block_table, const hkv_records* dst,
+                       const uint32_t* crc_out, int64_t* workspace_bytes) {
+  Geometry g;
+  PageView pv;
+  RecordView rv;
+  int64_t rb;
+  return quant_crc_check(fmt, shape, src, src_dtype, block_table, dst, crc_out, &g, &pv, &rv,
+                         &rb, workspace_bytes);
+}
+
+}  // namespace hkv
+
 extern "C" {
 
 int64_t hkv_record_bytes(int32_t fmt, int32_t block_tokens, int32_t n_kv_heads,

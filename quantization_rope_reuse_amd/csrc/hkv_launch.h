@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "hkv.h"
+
 namespace hkv {
 
 // Geometry of one call, after validation.
@@ -54,6 +56,12 @@ hipError_t launch_crc32(const Geometry& g, int64_t record_bytes, const RecordVie
 hipError_t launch_quant_crc_units(int fmt, int src_dtype, const Geometry& g, const PageView& src,
                                   const int32_t* table, const RecordView& dst,
                                   int64_t record_bytes, uint32_t* partials, hipStream_t stream);
+
+// Host-side argument checks of the fused put + CRC (hkv_quant_*_crc), all
+// but the workspace; on HKV_OK *workspace_bytes is the workspace it needs.
+int quant_crc_validate(int32_t fmt, const hkv_shape* shape, const hkv_pages* src,
+                       int32_t src_dtype, const int32_t* block_table, const hkv_records* dst,
+                       const uint32_t* crc_out, int64_t* workspace_bytes);
 
 hipError_t launch_crc32_merge(const Geometry& g, int64_t record_bytes, const RecordView& src,
                               const int32_t* table, int32_t num_pages, const uint32_t* partials,

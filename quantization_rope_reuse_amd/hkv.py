@@ -69,6 +69,18 @@ def declared_symbols():
     return sorted(set(re.findall(r"\b(hkv_[a-z0-9_]+)\s*\(", text)))
 
 
+def _header_define(name: str) -> int:
+    """An integer #define of include/hkv.h (e.g. HKV_NOALLOC_SCRATCH_BYTES)."""
+    with open(HEADER) as f:
+        m = re.search(r"#define\s+" + name + r"\s+\(?([0-9LL*\s]+)\)?", f.read())
+    if m is None:
+        raise KeyError(name)
+    value = 1
+    for factor in m.group(1).replace("LL", "").split("*"):
+        value *= int(factor)
+    return value
+
+
 def lib():
     global _lib
     if _lib is None:
@@ -83,6 +95,8 @@ def lib():
         l.hkv_quant_fp8_crc.argtypes = [P(Shape), P(Pages), ctypes.c_int32, vp, P(Records), vp,
                                         vp, ctypes.c_int64, vp]
         l.hkv_quant_int4_crc.argtypes = l.hkv_quant_fp8_crc.argtypes
+        l.hkv_quant_fp8_crc_noalloc.argtypes = [P(Shape), P(Pages), ctypes.c_int32, vp,
+                                                P(Records), vp, vp]
         l.hkv_quant_crc_workspace_bytes.argtypes = [P(Shape), ctypes.c_int32]
         l.hkv_quant_crc_workspace_bytes.restype = ctypes.c_int64
         l.hkv_fetch_dequant_rope_shift.argtypes = [
@@ -113,7 +127,8 @@ def lib():
         l.hkv_stream_destroy.argtypes = [vp]
         l.hkv_stream_destroy.restype = ctypes.c_int
         for name in ("hkv_quant_fp8", "hkv_quant_int4", "hkv_quant_fp8_crc",
-                     "hkv_quant_int4_crc", "hkv_fetch_dequant_rope_shift",
+                     "hkv_quant_int4_crc", "hkv_quant_fp8_crc_noalloc",
+                     "hkv_fetch_dequant_rope_shift",
                      "hkv_fetch_dequant_rope_shift_tokens", "hkv_crc32_blocks",
                      "hkv_page_visit_order", "hkv_token_drift", "hkv_select_top_tokens",
                      "hkv_frame_headers", "hkv_frame_verify", "hkv_frame_delta_m"):
@@ -287,6 +302,43 @@ def quant_crc(fmt, k_pages, v_pages, block_table, records, crc_out=None, workspa
                               _stream(stream, k_pages.device))
     _check(name, st)
     return crc_out
+
+
+NOALLOC_SCRATCH_BYTES = None     # HKV_NOALLOC_SCRATCH_BYTES, read from the header
+
+
+@_on_one_gpu
+def quant_fp8_crc_noalloc(k_pages, v_pages, block_table, records, crc_out, stream=None):
+    """hkv_quant_fp8_crc_noalloc: the FP8 put and the CRC-32 of every written
+    record in one pass, in the library's per-GPU scratch array (nothing is
+    allocated, here or in the library).  crc_out: a contiguous int32 tensor
+    of L * n_blocks elements (uint32 values), which the caller provides.
+    Shapes that need more than HKV_NOALLOC_SCRATCH_BYTES of scratch raise
+    HkvError (HKV_ERR_UNSUPPORTED) before anything runs.  Calls that overlap
+    in time on one GPU share its scratch and must not be made."""
+    pages, shp, dt = _pages(k_pages, v_pages)
+    L, _, tb, H, d = shp
+    nb = block_table.numel()
+    if records.shape[0] != L or records.shape[1] != nb:
+        raise ValueError("records must be [L, n_blocks, bytes] matching pages and table")
+    if crc_out.dtype != torch.int32 or not crc_out.is_contiguous() or crc_out.numel() != L * nb:
+        raise ValueError("crc_out must be a contiguous int32 tensor of L * n_blocks elements")
+    shape = Shape(L, nb, tb, H, d)
+    rec = _records(records, "fp8", tb, H)
+    st = lib().hkv_quant_fp8_crc_noalloc(ctypes.byref(shape), ctypes.byref(pages), dt,
+                                         _i32(block_table, "block_table"), ctypes.byref(rec),
+                                         ctypes.c_void_p(crc_out.data_ptr()),
+                                         _stream(stream, k_pages.device))
+    _check("hkv_quant_fp8_crc_noalloc", st)
+    return crc_out
+
+
+def noalloc_scratch_bytes() -> int:
+    """HKV_NOALLOC_SCRATCH_BYTES of include/hkv.h."""
+    global NOALLOC_SCRATCH_BYTES
+    if NOALLOC_SCRATCH_BYTES is None:
+        NOALLOC_SCRATCH_BYTES = _header_define("HKV_NOALLOC_SCRATCH_BYTES")
+    return NOALLOC_SCRATCH_BYTES
 
 
 def _fetch(name, records, fmt, block_table, delta, n_delta, rope_base, pairs, k_pages, v_pages,

@@ -20,7 +20,7 @@ def test_exports_every_declared_symbol():
                           "hkv_frame_delta_m", "hkv_select_workspace_bytes",
                           "hkv_quant_fp8_crc", "hkv_quant_int4_crc",
                           "hkv_quant_crc_workspace_bytes", "hkv_stream_probe",
-                          "hkv_stream_probe_put"}
+                          "hkv_stream_probe_put", "hkv_quant_fp8_crc_noalloc"}
     lib = H.lib()
     for n in names:
         assert getattr(lib, n) is not None
@@ -357,6 +357,37 @@ def test_fused_put_crc_rejects_bad_arguments():
     assert call(wsb=need - 1) == H.ERR_INVALID_ARG
     assert call(ws=FAKE + 4100) == H.ERR_INVALID_ARG               # misaligned
     assert call(sh=_shape(n_blocks=0), crc=0, ws=0, wsb=0) == H.OK
+
+
+def test_noalloc_put_crc_rejects_bad_arguments_and_oversized_shapes():
+    """hkv_quant_fp8_crc_noalloc checks its arguments like hkv_quant_fp8_crc
+    and refuses, before any HIP call, a shape whose scratch need exceeds
+    HKV_NOALLOC_SCRATCH_BYTES."""
+    lib = H.lib()
+    cap = H.noalloc_scratch_bytes()
+    assert cap == 32 * 1024 * 1024
+    p, r = _pages(), _recs()
+    call = lambda sh=_shape(), crc=FAKE, table=FAKE, rr=r: lib.hkv_quant_fp8_crc_noalloc(
+        ctypes.byref(sh), ctypes.byref(p), 0, ctypes.c_void_p(table), ctypes.byref(rr),
+        ctypes.c_void_p(crc), None)
+    assert call(crc=0) == H.ERR_INVALID_ARG
+    assert call(table=0) == H.ERR_INVALID_ARG
+    assert call(sh=_shape(head_dim=64)) == H.ERR_INVALID_ARG
+    assert call(rr=_recs(base=FAKE + 8)) == H.ERR_INVALID_ARG
+    # 80 layers x 1,024 blocks of 64 x 8 vectors: 341 MB of scratch needed
+    big = _shape(n_layers=80, n_blocks=1024, block_tokens=64, n_kv_heads=8)
+    rb = 133120
+    assert lib.hkv_quant_crc_workspace_bytes(ctypes.byref(big), 0) > cap
+    big_r = _recs(layer_stride_bytes=1024 * rb, block_stride_bytes=rb)
+    assert call(sh=big, rr=big_r) == H.ERR_UNSUPPORTED
+    # one such layer fits (4.3 MB); the largest fitting layer count is refused one above
+    one = _shape(n_layers=1, n_blocks=1024, block_tokens=64, n_kv_heads=8)
+    per_layer = lib.hkv_quant_crc_workspace_bytes(ctypes.byref(one), 0)
+    assert per_layer == 1024 * (rb // 128) * 4 <= cap
+    n_fit = cap // per_layer
+    over = _shape(n_layers=n_fit + 1, n_blocks=1024, block_tokens=64, n_kv_heads=8)
+    assert call(sh=over, rr=big_r) == H.ERR_UNSUPPORTED
+    assert call(sh=_shape(n_blocks=0), crc=0, table=0) == H.OK    # empty: nothing launched
 
 
 def test_binding_checks_record_size():

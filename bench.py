@@ -17,17 +17,27 @@ One step is one pass of the whole hot path over that cache:
 Inputs are resident in HBM before timing starts.
 
 Reported (one JSON line on stdout):
-  value        algorithmic bytes of the step / step time (GB/s, 1e9 B/s)
+  value        the metric: fetch GB/s = algorithmic fetch bytes of the 80
+               layers / the fetch phase's time in the timed steps (HIP events
+               on the fetch stream around its 80 launches)
+  ms_per_step  the whole step (put + CRC + 80 fetches); `step` gives its rate
   roofline     the fetch kernel (the dominant one): algorithmic bytes per
-               launch / mean launch time from HIP events on its stream,
-               against 8 TB/s HBM peak; `traffic` = HBM bytes per launch
-               measured with rocprofv3 counters for the current fetch source,
-               else null
-  fetch        fetch-only GB/s, fraction of peak, tokens/s
+               launch / mean launch time from the same HIP events, against
+               8 TB/s HBM peak; also the mean launch time of the committed
+               rocprofv3 kernel trace and the fraction it gives, while the
+               fetch sources match the ones profiled; `traffic` = HBM bytes
+               per launch from the committed rocprofv3 counters, likewise
+  fetch        fetch GB/s, fraction of peak, tokens/s
   put_crc      the fused put + CRC phase; put, crc32: the same work as two
                separate passes, timed outside the step
   ceiling      a plain streaming kernel with the fetch's 1:2 byte mix, and the
                fetch as a fraction of it
+  overlap      the layer-wise pipeline: records of all 80 layers in pinned
+               host memory, copied layer by layer into two staging buffers
+               and fetched from there (hkv_fetch_staged) while a compute
+               stream runs a synthetic suffix GEMM per layer gated on each
+               layer's fetch; exposed transfer + fetch time and the hidden
+               fraction
   cpu_baseline the CPU oracle on a bounded sample of the same workload
 
 Algorithmic bytes (what each step of the method covers):
@@ -86,6 +96,27 @@ def source_digest(*names):
         with open(os.path.join(ROOT, "quantization_rope_reuse_amd", "csrc", n), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
+
+
+def profiled_fetch_mean_ms():
+    """Mean duration (ms) of the Llama-3-70B-shaped fetch launch in the
+    committed rocprofv3 kernel trace, if it was taken on the current fetch
+    sources; else None."""
+    path = os.path.join(ROOT, "profiles", "llama3_70b_step_kernel_trace.md")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith((" ", "|", "(")):
+                key, _, val = line.partition(":")
+                fields[key.strip()] = val.strip()
+    if fields.get("source_digest") != source_digest("fetch.hip", "hkv_device.h"):
+        return None
+    try:
+        return float(fields["fetch_mean_us"]) / 1e3
+    except (KeyError, ValueError):
+        return None
 
 
 def measured_traffic():
@@ -217,12 +248,13 @@ def main():
     fetch_launch_bytes = vecs_per_layer * (130 + 256) + nb * 8
     fetch_bytes = L * fetch_launch_bytes
     step_bytes = put_bytes + crc_bytes + fetch_bytes
-    value = step_bytes / (ms_per_step * 1e-3) / 1e9
 
     mean_fetch_ms = float(np.mean(fetch_ms))
     achieved = fetch_launch_bytes / (mean_fetch_ms * 1e-3) / 1e9
     fetch_gbps = fetch_bytes / (float(np.mean(fetch_span_ms)) * 1e-3) / 1e9
     tokens_per_s = T / (float(np.mean(fetch_span_ms)) * 1e-3)
+    value = fetch_gbps                          # the metric: the fetch
+    prof_ms = profiled_fetch_mean_ms()
 
     # quick integrity check of the last step: no page left unwritten
     if bool(torch.isnan(out_k).any()) or bool(torch.isnan(out_v).any()):
@@ -271,6 +303,9 @@ def main():
                                 put_bytes, crc_bytes)
     put_ceiling = put_stream_ceiling(dev, hkv, separate["put"]["gbps"],
                                      put_bytes / (float(np.mean(put_crc_ms)) * 1e-3) / 1e9)
+    staged = None
+    if L == w.n_layers:
+        staged = staged_overlap(dev, hkv, w, L, records, ftab, dm, order)
     frames = frames_leg(dev, hkv, W, w, L, src_k, src_v, put_tab)
     select = recompute_select(dev, hkv, W)
     others = other_workloads(dev, hkv, W)
@@ -311,10 +346,18 @@ def main():
             "storage": "bf16 pages -> FP8 E4M3 records with fp16 scales -> bf16 pages "
                        "(arithmetic in fp32; per-block RoPE angles in fp64)",
             "layers": L, "tokens": T, "kv_heads": H, "head_dim": 128, "block_tokens": tb,
-            "step_bytes": step_bytes,
-            "step_bytes_without_crc_reads": put_bytes + fetch_bytes,
         },
-        "step_gbps_without_crc_reads": round((put_bytes + fetch_bytes) / (ms_per_step * 1e-3) / 1e9, 2),
+        "step": {
+            "ms": round(ms_per_step, 4),
+            "bytes": step_bytes,
+            "gbps": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 2),
+            "bytes_without_crc_reads": put_bytes + fetch_bytes,
+            "gbps_without_crc_reads": round((put_bytes + fetch_bytes) / (ms_per_step * 1e-3)
+                                            / 1e9, 2),
+            "note": "put + CRC32 of every record + 80 fetches; the CRC covers 10.9 GB of "
+                    "records that the fused pass reads from LDS, not HBM (left out in "
+                    "*_without_crc_reads)",
+        },
         "roofline": {
             "kernel": "fetch_kernel<fp8,bf16,half_split> (one layer per launch)",
             "bound": "hbm",
@@ -328,6 +371,11 @@ def main():
             "launch_ms_source": "HIP events on the fetch stream around the 80 per-layer "
                                 "launches of each timed step (and the one visit-order "
                                 "launch before them), divided by 80",
+            "profile_mean_launch_ms": None if prof_ms is None else round(prof_ms, 5),
+            "frac_at_profile_mean": None if prof_ms is None else round(
+                fetch_launch_bytes / (prof_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+            "profile": "profiles/llama3_70b_step_kernel_trace.md (rocprofv3 per-dispatch "
+                       "mean of the same launches; null when the fetch sources changed)",
         },
         "fetch": {
             "gbps": round(fetch_gbps, 1),
@@ -356,6 +404,7 @@ def main():
         "crc32": separate["crc32"],
         "other_workloads": others,
         "tp8_shard": shard,
+        "overlap": staged,
         "frames": frames,
         "recompute_select": select,
         "cpu_baseline": cpu,
@@ -636,6 +685,93 @@ def tp8_shard(dev, hkv, W, reps=5):
     return res
 
 
+def staged_overlap(dev, hkv, w, L, records, ftab, dm, order, suffix_tokens=2048, reps=3):
+    """The layer-wise pipeline of the HyperCache post (layer l+1 is brought
+    into a staging buffer while layer l's suffix tokens are computed) with a
+    real transfer: the FP8 records of all 80 layers sit in pinned host memory
+    and hkv_fetch_staged copies them layer by layer (DMA, copy stream) into
+    two device staging buffers and fetches each layer from there (fetch
+    stream).  The suffix compute is a synthetic bf16 GEMM with one
+    Llama-3-70B layer's weights ([S x 8192] @ [8192 x 106496], S suffix
+    tokens) per layer on a compute stream; layer l's GEMM waits on layer l's
+    ready event.  Timed with wall clock around each whole run (best of
+    `reps`): the transfer + fetch alone, the compute alone, and both
+    overlapped; exposed = overlapped - compute alone."""
+    import torch
+    nb, tb, H = w.n_blocks, w.block_tokens, w.n_kv_heads
+    rb = records.shape[2]
+    full = records.as_strided((L, nb, records.stride(1)), records.stride())
+    t0 = time.perf_counter()
+    host = torch.empty(full.shape, dtype=torch.uint8).pin_memory()
+    host.copy_(full)
+    host_rec = host[:, :, :rb]
+    staging = hkv.alloc_staging(nb, "fp8", tb, H, device=dev)
+    out_k = torch.empty((L, nb, tb, H, 128), dtype=torch.bfloat16, device=dev)
+    out_v = torch.empty_like(out_k)
+    x = torch.randn((suffix_tokens, 8192), dtype=torch.bfloat16, device=dev)
+    wt = torch.randn((8192, 106496), dtype=torch.bfloat16, device=dev) * 0.01
+    y = torch.empty((suffix_tokens, 106496), dtype=torch.bfloat16, device=dev)
+    copy_s, fetch_s, comp_s = (torch.cuda.Stream(device=dev) for _ in range(3))
+    ready = [torch.cuda.Event() for _ in range(L)]
+    torch.cuda.synchronize()
+    print(f"[bench] overlap leg: {host.numel() / 1e9:.2f} GB of records pinned in host memory "
+          f"({time.perf_counter() - t0:.1f} s)", file=sys.stderr, flush=True)
+
+    def staged():
+        hkv.fetch_staged(host_rec, "fp8", ftab, dm, w.rope_base, w.pairs, out_k, out_v, staging,
+                         visit_order=order, copy_stream=copy_s, fetch_stream=fetch_s,
+                         layer_ready=ready)
+
+    def compute(gated):
+        with torch.cuda.stream(comp_s):
+            for l in range(L):
+                if gated:
+                    comp_s.wait_event(ready[l])
+                torch.matmul(x, wt, out=y)
+
+    def timed(fn):
+        best = None
+        for _ in range(reps):
+            torch.cuda.synchronize()
+            t = time.perf_counter()
+            fn()
+            torch.cuda.synchronize()
+            dt = (time.perf_counter() - t) * 1e3
+            best = dt if best is None else min(best, dt)
+        return best
+
+    staged()
+    compute(False)
+    tf = timed(staged)
+    tc = timed(lambda: compute(False))
+    to = timed(lambda: (staged(), compute(True)))
+    # the pages of the overlapped run against a fetch from device memory
+    ok2 = torch.empty_like(out_k[:1])
+    ov2 = torch.empty_like(out_v[:1])
+    for l in (0, L - 1):
+        hkv.fetch_dequant_rope_shift(records[l:l + 1], "fp8", ftab, dm, w.rope_base, w.pairs,
+                                     ok2, ov2, visit_order=order)
+        if not (torch.equal(ok2[0], out_k[l]) and torch.equal(ov2[0], out_v[l])):
+            raise RuntimeError("the staged fetch disagrees with the fetch from device memory")
+    extent = (nb - 1) * host_rec.stride(1) + rb
+    exposed = to - tc
+    res = {
+        "workload": f"{L} layers of FP8 records ({L * extent / 1e9:.2f} GB) in pinned host "
+                    f"memory -> 2 staging buffers -> bf16 pages; suffix compute "
+                    f"[{suffix_tokens} x 8192] @ [8192 x 106496] bf16 per layer",
+        "transfer_fetch_ms": round(tf, 3),
+        "h2d_gbps": round(L * extent / (tf * 1e-3) / 1e9, 2),
+        "compute_ms": round(tc, 3),
+        "overlapped_ms": round(to, 3),
+        "serial_ms": round(tf + tc, 3),
+        "exposed_fetch_ms": round(exposed, 3),
+        "hidden_fraction": round(min(1.0, max(0.0, 1.0 - exposed / tf)), 4),
+    }
+    del host, host_rec, staging, out_k, out_v, x, wt, y, ok2, ov2
+    torch.cuda.empty_cache()
+    return res
+
+
 def frames_leg(dev, hkv, W, w, L, src_k, src_v, put_tab, reps=3):
     """The same cache as self-describing frames (64-byte header + record):
     put into the frames' records, CRC, header writing, and a full
@@ -847,6 +983,8 @@ def cpu_baseline(w, records_bytes, budget_s):
         "value": round(alg / wall / 1e9, 5),
         "unit": "GB/s",
         "cores": max(1, int(round(cpu_t / wall))),
+        "cores_available": len(os.sched_getaffinity(0)),
+        "host_cpus": os.cpu_count(),
         "kind": "oracle",
         "sample": f"put + CRC32 + fetch of {blocks} blocks ({blocks * tb} tokens, {layers} "
                   f"layer(s)) of the same workload, numpy float64 oracle, {wall:.1f} s wall, "

@@ -14,7 +14,8 @@
  *          paged KV buffer through a block table
  *          (hkv_fetch_dequant_rope_shift; one delta per token:
  *          hkv_fetch_dequant_rope_shift_tokens; a destination-ordered visit
- *          list: hkv_page_visit_order);
+ *          list: hkv_page_visit_order; layer by layer from host memory
+ *          through two staging buffers: hkv_fetch_staged);
  *   frame  a self-describing header in front of each record, its
  *          verification, and dm from the stored position (hkv_frame_*);
  *   select the tokens to recompute after a chunk reorder: per-token drift
@@ -39,7 +40,8 @@
  * - All array pointers are DEVICE pointers owned by the caller; the structs
  *   themselves are read from host memory during the call only.
  * - Calls are asynchronous on `stream` (0 = the default stream), allocate
- *   no memory (hkv_stream_pair_create aside, which creates two streams),
+ *   no memory (hkv_stream_pair_create aside, which creates two streams;
+ *   hkv_fetch_staged creates four events for the duration of the call),
  *   keep no state between calls and may be called from several host
  *   threads at once; hkv_quant_fp8_crc_noalloc is the one exception to the
  *   last two: it works in a scratch array the library keeps per GPU.
@@ -230,6 +232,44 @@ int hkv_fetch_dequant_rope_shift_tokens(const hkv_shape* shape, int32_t fmt,
                                         const int32_t* visit_order, double rope_base,
                                         int32_t pairs, const hkv_pages* dst, int32_t dst_dtype,
                                         hipStream_t stream);
+
+/* Records in host memory, one per (layer, logical block): record (l, b) at
+ *   host_base + l*layer_stride_bytes + b*block_stride_bytes
+ * (layout as hkv_records).  host_base and both strides: multiples of 16. */
+typedef struct {
+  const void* host_base;
+  int64_t layer_stride_bytes;
+  int64_t block_stride_bytes;
+} hkv_host_records;
+
+/* Layer-wise staged fetch (HyperCache post, Core Design, layer-wise transfer
+ * paragraph: layer l+1 is brought into a staging buffer while the GPU
+ * computes the suffix tokens of layer l).  For l = 0 .. n_layers-1: copies
+ * layer l's records, the bytes [0, (n_blocks-1)*block_stride_bytes +
+ * hkv_record_bytes()) of the layer, from host memory into staging buffer
+ * l mod 2 on copy_stream (DMA), then runs hkv_fetch_dequant_rope_shift on
+ * that one layer on fetch_stream into layer l of `dst`, with the same
+ * table, deltas, visit order, base and pairs for every layer.  A layer's
+ * fetch waits for its copy; a buffer is refilled only after the fetch that
+ * read it has run (and, for the first two copies, after the work enqueued on
+ * fetch_stream before the call).  layer_ready: NULL, or n_layers events
+ * created by the caller (NULL entries are skipped); event l is recorded on
+ * fetch_stream after layer l's fetch, so a compute stream that waits on it
+ * sees layer l's pages.  The call creates four events for its own use and
+ * allocates no memory.
+ * src: host memory the copies read until fetch_stream has passed the last
+ * layer; pinned (hipHostMalloc) for the copies to run asynchronously.
+ * staging0, staging1: distinct device buffers of staging_bytes >= one
+ * layer's extent above, 16-byte aligned, not used by anything else until
+ * fetch_stream has passed the last layer.  When that point of fetch_stream
+ * completes, every copy and fetch of the call has completed.  copy_stream
+ * and fetch_stream may be the same stream (no overlap then). */
+int hkv_fetch_staged(const hkv_shape* shape, int32_t fmt, const hkv_host_records* src,
+                     void* staging0, void* staging1, int64_t staging_bytes,
+                     const int32_t* block_table, const int32_t* delta_m,
+                     const int32_t* visit_order, double rope_base, int32_t pairs,
+                     const hkv_pages* dst, int32_t dst_dtype, hipStream_t copy_stream,
+                     hipStream_t fetch_stream, hipEvent_t* layer_ready);
 
 /* Visiting order for hkv_fetch_dequant_rope_shift: writes to order_out
  * (int32 [n_blocks], device) the logical blocks sorted by destination page

@@ -23,7 +23,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libhkv.so")
 SOURCES = ("api.hip", "quant.hip", "fetch.hip", "crc.hip", "order.hip", "streams.hip",
-           "select.hip", "frames.hip", "probe.hip", "noalloc.hip")
+           "select.hip", "frames.hip", "probe.hip", "noalloc.hip",
+           "staged.hip")
 ARCH = "gfx950"
 
 

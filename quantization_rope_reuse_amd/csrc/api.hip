@@ -185,26 +185,33 @@ int fetch_common(const hkv_shape* shape, int32_t fmt, const hkv_records* src,
                  const int32_t* block_table, const int32_t* delta_m, bool per_token,
                  const int32_t* visit_order, double rope_base, int32_t pairs,
                  const hkv_pages* dst, int32_t dst_dtype, hipStream_t stream) {
-  Geometry g;
-  PageView pv;
-  RecordView rv;
-  int st;
-  if (!valid_format(fmt)) return HKV_ERR_INVALID_ARG;
-  if ((st = check_shape(shape, &g)) != HKV_OK) return st;
-  if ((st = check_records(src, fmt, shape, &rv)) != HKV_OK) return st;
-  if ((st = check_pages(dst, dst_dtype, &pv)) != HKV_OK) return st;
-  if (pairs != HKV_ROPE_INTERLEAVED && pairs != HKV_ROPE_HALF_SPLIT) return HKV_ERR_INVALID_ARG;
-  if (!(rope_base > 0.0) || !isfinite(rope_base)) return HKV_ERR_INVALID_ARG;
-  if ((!block_table || !delta_m) && g.n_blocks > 0) return HKV_ERR_INVALID_ARG;
-  if (g.n_layers == 0 || g.n_blocks == 0) return HKV_OK;
-  return to_status(hkv::launch_fetch(fmt, dst_dtype, pairs, g, rv, block_table, delta_m,
-                                     per_token, visit_order, rope_base, pv, stream));
+  hkv::FetchViews f;
+  const int st = hkv::fetch_check(shape, fmt, src, block_table, delta_m, rope_base, pairs, dst,
+                                  dst_dtype, &f);
+  if (st != HKV_OK) return st;
+  if (f.g.n_layers == 0 || f.g.n_blocks == 0) return HKV_OK;
+  return to_status(hkv::launch_fetch(fmt, dst_dtype, pairs, f.g, f.rv, block_table, delta_m,
+                                     per_token, visit_order, rope_base, f.pv, stream));
 }
 
 
 }  // namespace
 
 namespace hkv {
+
+int fetch_check(const hkv_shape* shape, int32_t fmt, const hkv_records* src,
+                const int32_t* block_table, const int32_t* delta_m, double rope_base,
+                int32_t pairs, const hkv_pages* dst, int32_t dst_dtype, FetchViews* f) {
+  int st;
+  if (!valid_format(fmt)) return HKV_ERR_INVALID_ARG;
+  if ((st = check_shape(shape, &f->g)) != HKV_OK) return st;
+  if ((st = check_records(src, fmt, shape, &f->rv)) != HKV_OK) return st;
+  if ((st = check_pages(dst, dst_dtype, &f->pv)) != HKV_OK) return st;
+  if (pairs != HKV_ROPE_INTERLEAVED && pairs != HKV_ROPE_HALF_SPLIT) return HKV_ERR_INVALID_ARG;
+  if (!(rope_base > 0.0) || !isfinite(rope_base)) return HKV_ERR_INVALID_ARG;
+  if ((!block_table || !delta_m) && f->g.n_blocks > 0) return HKV_ERR_INVALID_ARG;
+  return HKV_OK;
+}
 
 int quant_crc_validate(int32_t fmt, const hkv_shape* shape, const hkv_pages* src,
                        int32_t src_dtype, const int32_t* block_table, const hkv_records* dst,

@@ -57,6 +57,16 @@ hipError_t launch_quant_crc_units(int fmt, int src_dtype, const Geometry& g, con
                                   const int32_t* table, const RecordView& dst,
                                   int64_t record_bytes, uint32_t* partials, hipStream_t stream);
 
+// Validated views of one fetch call (hkv_fetch_dequant_rope_shift's checks).
+struct FetchViews {
+  Geometry g;
+  RecordView rv;
+  PageView pv;
+};
+int fetch_check(const hkv_shape* shape, int32_t fmt, const hkv_records* src,
+                const int32_t* block_table, const int32_t* delta_m, double rope_base,
+                int32_t pairs, const hkv_pages* dst, int32_t dst_dtype, FetchViews* views);
+
 // Host-side argument checks of the fused put + CRC (hkv_quant_*_crc), all
 // but the workspace; on HKV_OK *workspace_bytes is the workspace it needs.
 int quant_crc_validate(int32_t fmt, const hkv_shape* shape, const hkv_pages* src,

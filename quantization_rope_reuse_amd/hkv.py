@@ -58,6 +58,11 @@ class Records(ctypes.Structure):
                 ("block_stride_bytes", ctypes.c_int64)]
 
 
+class HostRecords(ctypes.Structure):
+    _fields_ = [("host_base", ctypes.c_void_p), ("layer_stride_bytes", ctypes.c_int64),
+                ("block_stride_bytes", ctypes.c_int64)]
+
+
 _lib = None
 
 
@@ -105,6 +110,9 @@ def lib():
         l.hkv_fetch_dequant_rope_shift_tokens.argtypes = [
             P(Shape), ctypes.c_int32, P(Records), vp, vp, vp, ctypes.c_double, ctypes.c_int32,
             P(Pages), ctypes.c_int32, vp]
+        l.hkv_fetch_staged.argtypes = [
+            P(Shape), ctypes.c_int32, P(HostRecords), vp, vp, ctypes.c_int64, vp, vp, vp,
+            ctypes.c_double, ctypes.c_int32, P(Pages), ctypes.c_int32, vp, vp, vp]
         l.hkv_page_visit_order.argtypes = [vp, ctypes.c_int32, ctypes.c_int32, vp, vp]
         l.hkv_crc32_blocks.argtypes = [P(Shape), ctypes.c_int32, P(Records), vp, vp]
         l.hkv_token_drift.argtypes = [vp, vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
@@ -129,7 +137,8 @@ def lib():
         for name in ("hkv_quant_fp8", "hkv_quant_int4", "hkv_quant_fp8_crc",
                      "hkv_quant_int4_crc", "hkv_quant_fp8_crc_noalloc",
                      "hkv_fetch_dequant_rope_shift",
-                     "hkv_fetch_dequant_rope_shift_tokens", "hkv_crc32_blocks",
+                     "hkv_fetch_dequant_rope_shift_tokens", "hkv_fetch_staged",
+                     "hkv_crc32_blocks",
                      "hkv_page_visit_order", "hkv_token_drift", "hkv_select_top_tokens",
                      "hkv_frame_headers", "hkv_frame_verify", "hkv_frame_delta_m"):
             getattr(l, name).restype = ctypes.c_int
@@ -379,6 +388,79 @@ def fetch_dequant_rope_shift_tokens(records, fmt, block_table, delta_m_tokens, r
     return _fetch("hkv_fetch_dequant_rope_shift_tokens", records, fmt, block_table,
                   delta_m_tokens, lambda nb, tb: nb * tb, rope_base, pairs, k_pages, v_pages,
                   visit_order, stream)
+
+
+def fetch_staged(host_records, fmt, block_table, delta_m, rope_base, pairs, k_pages, v_pages,
+                 staging, visit_order=None, copy_stream=None, fetch_stream=None,
+                 layer_ready=None):
+    """Layer-by-layer fetch from host memory through two staging buffers
+    (hkv_fetch_staged): layer l's records are copied from host_records (a
+    pinned CPU uint8 tensor [L, n_blocks, >= record_bytes]) into staging[l %
+    2] on copy_stream, then fetched into layer l of k/v_pages on
+    fetch_stream.  staging: two device uint8 tensors, each holding one
+    layer's records.  layer_ready: None or L torch.cuda.Event objects,
+    recorded on fetch_stream after each layer's fetch.  Streams default to
+    the current one (copies and fetches then do not overlap)."""
+    if not isinstance(host_records, torch.Tensor) or host_records.device.type != "cpu":
+        raise ValueError("host_records must be a CPU tensor")
+    if not host_records.is_pinned():
+        raise ValueError("host_records must be in pinned host memory (pin_memory())")
+    if host_records.dim() != 3 or host_records.stride(2) != 1 or host_records.dtype != torch.uint8:
+        raise ValueError("host_records must be a uint8 [L, n_blocks, bytes] tensor, last axis "
+                         "contiguous")
+    if len(staging) != 2:
+        raise ValueError("staging must be two device buffers")
+    dev = k_pages.device
+    for t in (block_table, delta_m, k_pages, v_pages, *staging,
+              *(() if visit_order is None else (visit_order,))):
+        if not isinstance(t, torch.Tensor) or t.device != dev or dev.type != "cuda":
+            raise ValueError("staging, tables and pages must be tensors on one GPU")
+    pages, shp, dt = _pages(k_pages, v_pages)
+    L, _, tb, H, d = shp
+    nb = block_table.numel()
+    if host_records.shape[0] != L or host_records.shape[1] != nb or delta_m.numel() != nb:
+        raise ValueError("host records [L, n_blocks, bytes], pages, table and deltas must agree")
+    need = record_bytes(fmt, tb, H)
+    if host_records.shape[2] < need:
+        raise ValueError(f"host records hold {host_records.shape[2]} bytes per block; "
+                         f"needs {need}")
+    extent = (nb - 1) * host_records.stride(1) + need
+    for b in staging:
+        if b.dtype != torch.uint8 or not b.is_contiguous() or b.numel() < extent:
+            raise ValueError(f"each staging buffer must be a contiguous uint8 tensor of at "
+                             f"least {extent} bytes")
+    if visit_order is not None and visit_order.numel() != nb:
+        raise ValueError("visit_order must hold n_blocks entries")
+    fetch_stream = fetch_stream or torch.cuda.current_stream(dev)
+    copy_stream = copy_stream or fetch_stream
+    events = None
+    if layer_ready is not None:
+        if len(layer_ready) != L:
+            raise ValueError("layer_ready must hold one event per layer")
+        for ev in layer_ready:
+            if not ev.cuda_event:            # torch creates its events on first record
+                ev.record(fetch_stream)
+        events = (ctypes.c_void_p * L)(*[ev.cuda_event for ev in layer_ready])
+    shape = Shape(L, nb, tb, H, d)
+    hr = HostRecords(host_records.data_ptr(), host_records.stride(0), host_records.stride(1))
+    order = None if visit_order is None else _i32(visit_order, "visit_order")
+    st = lib().hkv_fetch_staged(
+        ctypes.byref(shape), FORMATS[fmt], ctypes.byref(hr),
+        ctypes.c_void_p(staging[0].data_ptr()), ctypes.c_void_p(staging[1].data_ptr()),
+        min(staging[0].numel(), staging[1].numel()), _i32(block_table, "block_table"),
+        _i32(delta_m, "delta_m"), order, float(rope_base), PAIRS[pairs], ctypes.byref(pages),
+        dt, _stream(copy_stream, dev), _stream(fetch_stream, dev),
+        None if events is None else ctypes.cast(events, ctypes.c_void_p))
+    _check("hkv_fetch_staged", st)
+    return k_pages, v_pages
+
+
+def alloc_staging(n_blocks: int, fmt, block_tokens: int, n_kv_heads: int, device="cuda"):
+    """Two device buffers, each holding one layer of records laid out as
+    alloc_records lays them out (block stride rounded up to 16 bytes)."""
+    stride = (record_bytes(fmt, block_tokens, n_kv_heads) + 15) // 16 * 16
+    return tuple(torch.empty(n_blocks * stride, dtype=torch.uint8, device=device)
+                 for _ in range(2))
 
 
 @_on_one_gpu

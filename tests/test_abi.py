@@ -20,7 +20,8 @@ def test_exports_every_declared_symbol():
                           "hkv_frame_delta_m", "hkv_select_workspace_bytes",
                           "hkv_quant_fp8_crc", "hkv_quant_int4_crc",
                           "hkv_quant_crc_workspace_bytes", "hkv_stream_probe",
-                          "hkv_stream_probe_put", "hkv_quant_fp8_crc_noalloc"}
+                          "hkv_stream_probe_put", "hkv_quant_fp8_crc_noalloc",
+                          "hkv_fetch_staged"}
     lib = H.lib()
     for n in names:
         assert getattr(lib, n) is not None
@@ -388,6 +389,50 @@ def test_noalloc_put_crc_rejects_bad_arguments_and_oversized_shapes():
     over = _shape(n_layers=n_fit + 1, n_blocks=1024, block_tokens=64, n_kv_heads=8)
     assert call(sh=over, rr=big_r) == H.ERR_UNSUPPORTED
     assert call(sh=_shape(n_blocks=0), crc=0, table=0) == H.OK    # empty: nothing launched
+
+
+def test_staged_fetch_rejects_bad_arguments():
+    """hkv_fetch_staged validates everything on the host before it creates an
+    event or enqueues a copy."""
+    lib = H.lib()
+    s, p = _shape(), _pages()
+    rb = 33280
+
+    def call(sh=s, host=FAKE, ls=4 * rb, bs=rb, s0=FAKE + (1 << 24), s1=FAKE + (1 << 25),
+             sb=4 * rb, table=FAKE, dm=FAKE, base=1e4, pairs=0, fmt=0, dt=0):
+        hr = H.HostRecords(host, ls, bs)
+        return lib.hkv_fetch_staged(ctypes.byref(sh), fmt, ctypes.byref(hr), ctypes.c_void_p(s0),
+                                    ctypes.c_void_p(s1), sb, ctypes.c_void_p(table),
+                                    ctypes.c_void_p(dm), None, base, pairs, ctypes.byref(p), dt,
+                                    None, None, None)
+    assert call(host=0) == H.ERR_INVALID_ARG
+    assert call(host=FAKE + 8) == H.ERR_INVALID_ARG
+    assert call(s0=0) == H.ERR_INVALID_ARG
+    assert call(s1=FAKE + (1 << 24)) == H.ERR_INVALID_ARG          # the same buffer twice
+    assert call(s1=FAKE + 8) == H.ERR_INVALID_ARG
+    assert call(sb=4 * rb - 16) == H.ERR_INVALID_ARG               # smaller than one layer
+    assert call(bs=rb - 16) == H.ERR_INVALID_ARG
+    assert call(ls=3 * rb) == H.ERR_INVALID_ARG                     # layers overlap
+    assert call(ls=-16) == H.ERR_INVALID_ARG
+    assert call(fmt=5) == H.ERR_INVALID_ARG
+    assert call(base=0.0) == H.ERR_INVALID_ARG
+    assert call(pairs=3) == H.ERR_INVALID_ARG
+    assert call(table=0) == H.ERR_INVALID_ARG
+    assert call(dm=0) == H.ERR_INVALID_ARG
+    assert call(dt=7) == H.ERR_INVALID_ARG
+    assert call(sh=_shape(head_dim=64)) == H.ERR_INVALID_ARG
+    assert call(sh=_shape(n_layers=0)) == H.OK                      # empty: nothing enqueued
+    assert call(sh=_shape(n_blocks=0), table=0, dm=0) == H.OK
+
+
+def test_staged_binding_checks_host_memory():
+    import torch
+    k = torch.zeros((1, 4, 16, 8, 128), dtype=torch.bfloat16)
+    host = torch.zeros((1, 4, 33280), dtype=torch.uint8)           # not pinned (no GPU here)
+    with pytest.raises(ValueError, match="pinned"):
+        H.fetch_staged(host, "fp8", torch.zeros(4, dtype=torch.int32),
+                       torch.zeros(4, dtype=torch.int32), 1e4, "interleaved", k, k,
+                       (torch.zeros(1, dtype=torch.uint8),) * 2)
 
 
 def test_binding_checks_record_size():

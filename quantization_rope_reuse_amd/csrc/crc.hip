@@ -171,6 +171,8 @@ struct MergeParams {
   uint32_t init_term;          // 0xFFFFFFFF * x^(8 * record bytes) mod P
 };
 
+constexpr int kMergeBatch = 24;
+
 // One record's CRC in one wave (see above).
 __device__ __forceinline__ void merge_record(const MergeParams& p, const uint32_t (*M)[256],
                                              const uint32_t (*T)[256], int r, int lane) {
@@ -187,17 +189,19 @@ __device__ __forceinline__ void merge_record(const MergeParams& p, const uint32_
   const uint32_t scale_k = p.scale_shift[lane];
   const int n = p.code_units / kWave;            // code units per lane
   const int words = per_lane / 4;                 // scale words per lane
-  // Batches of 8 of each: a batch's 16 loads are issued before either chain
-  // consumes them (the batch guards are uniform over the wave).
+  // Batches of kMergeBatch of each: a batch's loads are all issued before
+  // either chain consumes them (one batch for up to 24 code units and 96
+  // scale bytes per lane; the batch guards are uniform over the wave).
   uint32_t c = 0, sreg = 0;
-  for (int j0 = 0; j0 < n || j0 < words; j0 += 8) {
-    uint32_t w[8], x[8];
+  for (int j0 = 0; j0 < n || j0 < words; j0 += kMergeBatch) {
+    uint32_t w[kMergeBatch], x[kMergeBatch];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) w[i] = j0 + i < n ? part[static_cast<int64_t>(kWave) * (j0 + i)] : 0u;
+    for (int i = 0; i < kMergeBatch; ++i)
+      w[i] = j0 + i < n ? part[static_cast<int64_t>(kWave) * (j0 + i)] : 0u;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) x[i] = j0 + i < words ? sc[j0 + i] : 0u;
+    for (int i = 0; i < kMergeBatch; ++i) x[i] = j0 + i < words ? sc[j0 + i] : 0u;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < kMergeBatch; ++i) {
       if (j0 + i < n)
         c = M[0][c & 0xFFu] ^ M[1][(c >> 8) & 0xFFu] ^ M[2][(c >> 16) & 0xFFu] ^ M[3][c >> 24] ^
             w[i];

@@ -20,10 +20,10 @@
 //   faster than four passes at the Llama-3-70B and Qwen3-8B shapes;
 // * the INT4 put makes four (chunks of 128) when the block's vector count is a
 //   multiple of 128, else two: one pass is 10-20% slower, two 5% slower;
-// * the fused put + CRC makes two passes for FP8 from 16-bit sources (1% faster
-//   than four; with one pass its CRC tail, which holds the workgroup's LDS
-//   after the loads, follows every 8 KB of source: 12% slower) and four (or
-//   two) for INT4;
+// * the fused put + CRC makes four (or two) as well: with one pass its CRC
+//   tail, which holds the workgroup's LDS after the loads, follows every 8 KB
+//   of source (12% slower); two passes measured within 3% either way
+//   (Llama-3-70B shape 0.6% faster, Qwen3-8B shape 3% slower);
 // * the FP8 put from fp32 sources (small workloads only) keeps four or two.
 #include "crc_device.h"
 #include "hkv_device.h"
@@ -169,14 +169,15 @@ __device__ __forceinline__ uint32_t quant_vector(float (&a)[8], float (&b)[8], u
 // are non-temporal.
 //
 // CRC (fused put + CRC-32, chunks of exactly 32 * PASSES vectors): the
-// workgroup's codes form a contiguous run of the record (8 KB: FP8 with two
-// passes, INT4 with four), staged in LDS as they are written; after a
-// barrier one thread per 128-byte unit (64 units: exactly the first wave;
-// the other waves end there) feeds its unit into a zero CRC register (byte
-// tables in LDS) and stores that raw value in `partials` at the unit's index
-// in the record.  A workgroup in this tail holds one wave slot besides its
-// LDS; measured variants that kept a second wave (for the scale units) or
-// gave a lane a second chain ran 5-6% slower.  The byte tables are built
+// workgroup's codes form a contiguous run of the record (16 KB FP8, 8 KB INT4
+// with four passes), staged in LDS as they are written; after a barrier one
+// thread per 128-byte unit (128 FP8 units: the first two waves; 64 INT4
+// units: the first wave; the other waves end there) feeds its unit into a
+// zero CRC register (byte tables in LDS) and stores that raw value in
+// `partials` at the unit's index in the record.  A workgroup in this tail
+// holds its LDS and the chain waves' slots: measured variants that kept one
+// more wave (for the scale units) or gave a lane a second chain ran 5-6%
+// slower.  The byte tables are built
 // while the source loads are in flight.  The scale units at the end of the
 // record are left to the merge kernel (crc.hip), which reads them back: one
 // more thread here for the chunk's scale unit would run a whole further
@@ -281,15 +282,12 @@ hipError_t launch_passes(QuantParams p, const Geometry& g, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// The FP8 put from 16-bit sources makes one pass (two when fused with the
-// CRC); otherwise four passes when the block's vectors fill chunks of 128,
-// else two (the fused path requires whole chunks: vecs % 64 == 0, checked by
-// the caller).
+// One pass for the FP8 put from 16-bit sources; otherwise four passes when
+// the block's vectors fill chunks of 128, else two (the fused path requires
+// whole chunks: vecs % 64 == 0, checked by the caller).
 template <int FMT, int SDT, bool CRC>
 hipError_t launch_t(const QuantParams& p, const Geometry& g, hipStream_t stream) {
-  if constexpr (FMT == kFP8 && SDT != kF32 && CRC)
-    return launch_passes<FMT, SDT, CRC, 2>(p, g, stream);
-  else if constexpr (FMT == kFP8 && SDT != kF32)
+  if constexpr (FMT == kFP8 && SDT != kF32 && !CRC)
     return launch_passes<FMT, SDT, CRC, 1>(p, g, stream);
   else
     return g.vecs % 128 == 0 ? launch_passes<FMT, SDT, CRC, 4>(p, g, stream)

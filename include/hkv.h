@@ -160,13 +160,22 @@ int hkv_quant_int4(const hkv_shape* shape, const hkv_pages* src, int32_t src_dty
  * workspace: 16-byte aligned device memory of at least
  * hkv_quant_crc_workspace_bytes() bytes (4 bytes per 128 bytes of records);
  * when block_tokens * n_kv_heads is not a multiple of 64 that is 0, no
- * workspace is needed and the call runs the put and then the CRC kernel. */
+ * workspace is needed and the call runs the put and then the CRC kernel.
+ * records_ready: NULL, or an event (created by the caller) that the call
+ * records on `stream` once the put has written the records and before the
+ * CRC work that follows it: work that needs only the records (a fetch on
+ * another stream) can wait on it instead of on the whole call, so the
+ * merge of the CRCs overlaps it.  The CRCs are complete when `stream`
+ * reaches the end of the call.  An event with timing enabled times the put
+ * phase. */
 int hkv_quant_fp8_crc(const hkv_shape* shape, const hkv_pages* src, int32_t src_dtype,
                       const int32_t* block_table, const hkv_records* dst, uint32_t* crc_out,
-                      void* workspace, int64_t workspace_bytes, hipStream_t stream);
+                      void* workspace, int64_t workspace_bytes, hipStream_t stream,
+                      hipEvent_t records_ready);
 int hkv_quant_int4_crc(const hkv_shape* shape, const hkv_pages* src, int32_t src_dtype,
                        const int32_t* block_table, const hkv_records* dst, uint32_t* crc_out,
-                       void* workspace, int64_t workspace_bytes, hipStream_t stream);
+                       void* workspace, int64_t workspace_bytes, hipStream_t stream,
+                       hipEvent_t records_ready);
 
 /* Workspace bytes for hkv_quant_*_crc with this shape and format; -1 on bad
  * arguments. */
@@ -175,7 +184,8 @@ int64_t hkv_quant_crc_workspace_bytes(const hkv_shape* shape, int32_t fmt);
 /* hkv_quant_fp8_crc for callers that cannot allocate device memory (code
  * under HIP graph capture, serving loops that never call the allocator,
  * harnesses that forbid it).  Same arguments, records and CRCs as
- * hkv_quant_fp8_crc, without the workspace: the call uses a scratch array
+ * hkv_quant_fp8_crc, without the workspace (and records no records_ready
+ * event): the call uses a scratch array
  * of HKV_NOALLOC_SCRATCH_BYTES that the library holds in device memory, one
  * per GPU it runs on, for the life of the process, and calls no allocator.
  * A shape whose hkv_quant_crc_workspace_bytes(shape, HKV_FP8_E4M3) exceeds

@@ -153,10 +153,19 @@ int quant_crc_check(int32_t fmt, const hkv_shape* shape, const hkv_pages* src,
   return HKV_OK;
 }
 
+// Records the caller's records_ready event, if any, on the call's stream.
+int record_ready(hipEvent_t records_ready, hipStream_t stream) {
+  if (records_ready && hipEventRecord(records_ready, stream) != hipSuccess) {
+    (void)hipGetLastError();
+    return HKV_ERR_HIP;
+  }
+  return HKV_OK;
+}
+
 int quant_crc_common(int32_t fmt, const hkv_shape* shape, const hkv_pages* src,
                      int32_t src_dtype, const int32_t* block_table, const hkv_records* dst,
                      uint32_t* crc_out, void* workspace, int64_t workspace_bytes,
-                     hipStream_t stream) {
+                     hipStream_t stream, hipEvent_t records_ready) {
   Geometry g;
   PageView pv;
   RecordView rv;
@@ -166,10 +175,12 @@ int quant_crc_common(int32_t fmt, const hkv_shape* shape, const hkv_pages* src,
   if (st != HKV_OK) return st;
   if (need > 0 && (!workspace || !aligned16(workspace) || workspace_bytes < need))
     return HKV_ERR_INVALID_ARG;
-  if (g.n_layers == 0 || g.n_blocks == 0) return HKV_OK;
+  if (g.n_layers == 0 || g.n_blocks == 0) return record_ready(records_ready, stream);
   if (need == 0) {
     const hipError_t e = hkv::launch_quant(fmt, src_dtype, g, pv, block_table, rv, stream);
     if (e != hipSuccess) return HKV_ERR_HIP;
+    const int st_ready = record_ready(records_ready, stream);
+    if (st_ready != HKV_OK) return st_ready;
     // the CRCs of skipped blocks stay unchanged, as on the one-pass path
     return to_status(hkv::launch_crc32(g, rb, rv, block_table, pv.num_pages, crc_out, stream));
   }
@@ -177,6 +188,8 @@ int quant_crc_common(int32_t fmt, const hkv_shape* shape, const hkv_pages* src,
   const hipError_t e = hkv::launch_quant_crc_units(fmt, src_dtype, g, pv, block_table, rv, rb,
                                                    partials, stream);
   if (e != hipSuccess) return HKV_ERR_HIP;
+  const int st_ready = record_ready(records_ready, stream);
+  if (st_ready != HKV_OK) return st_ready;
   return to_status(hkv::launch_crc32_merge(g, rb, rv, block_table, pv.num_pages, partials,
                                            crc_out, stream));
 }
@@ -267,16 +280,18 @@ int64_t hkv_quant_crc_workspace_bytes(const hkv_shape* shape, int32_t fmt) {
 
 int hkv_quant_fp8_crc(const hkv_shape* shape, const hkv_pages* src, int32_t src_dtype,
                       const int32_t* block_table, const hkv_records* dst, uint32_t* crc_out,
-                      void* workspace, int64_t workspace_bytes, hipStream_t stream) {
+                      void* workspace, int64_t workspace_bytes, hipStream_t stream,
+                      hipEvent_t records_ready) {
   return quant_crc_common(HKV_FP8_E4M3, shape, src, src_dtype, block_table, dst, crc_out,
-                          workspace, workspace_bytes, stream);
+                          workspace, workspace_bytes, stream, records_ready);
 }
 
 int hkv_quant_int4_crc(const hkv_shape* shape, const hkv_pages* src, int32_t src_dtype,
                        const int32_t* block_table, const hkv_records* dst, uint32_t* crc_out,
-                       void* workspace, int64_t workspace_bytes, hipStream_t stream) {
+                       void* workspace, int64_t workspace_bytes, hipStream_t stream,
+                       hipEvent_t records_ready) {
   return quant_crc_common(HKV_INT4, shape, src, src_dtype, block_table, dst, crc_out,
-                          workspace, workspace_bytes, stream);
+                          workspace, workspace_bytes, stream, records_ready);
 }
 
 int hkv_fetch_dequant_rope_shift(const hkv_shape* shape, int32_t fmt, const hkv_records* src,

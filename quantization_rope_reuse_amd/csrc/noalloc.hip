@@ -76,5 +76,5 @@ extern "C" int hkv_quant_fp8_crc_noalloc(const hkv_shape* shape, const hkv_pages
     if (st != HKV_OK) return st;
   }
   return hkv_quant_fp8_crc(shape, src, src_dtype, block_table, dst, crc_out, ws,
-                           ws ? kScratchBytes : 0, stream);
+                           ws ? kScratchBytes : 0, stream, nullptr);
 }

@@ -98,7 +98,7 @@ def lib():
         l.hkv_quant_fp8.argtypes = [P(Shape), P(Pages), ctypes.c_int32, vp, P(Records), vp]
         l.hkv_quant_int4.argtypes = [P(Shape), P(Pages), ctypes.c_int32, vp, P(Records), vp]
         l.hkv_quant_fp8_crc.argtypes = [P(Shape), P(Pages), ctypes.c_int32, vp, P(Records), vp,
-                                        vp, ctypes.c_int64, vp]
+                                        vp, ctypes.c_int64, vp, vp]
         l.hkv_quant_int4_crc.argtypes = l.hkv_quant_fp8_crc.argtypes
         l.hkv_quant_fp8_crc_noalloc.argtypes = [P(Shape), P(Pages), ctypes.c_int32, vp,
                                                 P(Records), vp, vp]
@@ -282,11 +282,14 @@ def quant_crc_workspace_bytes(fmt, n_layers: int, n_blocks: int, block_tokens: i
 
 @_on_one_gpu
 def quant_crc(fmt, k_pages, v_pages, block_table, records, crc_out=None, workspace=True,
-              stream=None):
+              stream=None, records_ready=None):
     """Put (FP8 or INT4) and the CRC-32 of every written record in one pass.
     Returns crc_out, an int32 tensor [L, n_blocks] holding uint32 values.
     workspace: True (allocated here), or a uint8 tensor of at least
-    quant_crc_workspace_bytes bytes."""
+    quant_crc_workspace_bytes bytes.  records_ready: None, or a
+    torch.cuda.Event that the library records on the stream once the
+    records are written, before the CRC merge (other streams that need only
+    the records wait on it)."""
     pages, shp, dt = _pages(k_pages, v_pages)
     L, _, tb, H, d = shp
     nb = block_table.numel()
@@ -303,12 +306,17 @@ def quant_crc(fmt, k_pages, v_pages, block_table, records, crc_out=None, workspa
         raise ValueError("workspace must be a contiguous uint8 tensor")
     shape = Shape(L, nb, tb, H, d)
     rec = _records(records, fmt, tb, H)
+    hs = _stream(stream, k_pages.device)
+    ready = None
+    if records_ready is not None:
+        if not records_ready.cuda_event:     # torch creates its events on first record
+            records_ready.record(torch.cuda.current_stream(k_pages.device))
+        ready = ctypes.c_void_p(records_ready.cuda_event)
     name = "hkv_quant_fp8_crc" if FORMATS[fmt] == FP8_E4M3 else "hkv_quant_int4_crc"
     st = getattr(lib(), name)(ctypes.byref(shape), ctypes.byref(pages), dt,
                               _i32(block_table, "block_table"), ctypes.byref(rec),
                               ctypes.c_void_p(crc_out.data_ptr()),
-                              ctypes.c_void_p(workspace.data_ptr()), workspace.numel(),
-                              _stream(stream, k_pages.device))
+                              ctypes.c_void_p(workspace.data_ptr()), workspace.numel(), hs, ready)
     _check(name, st)
     return crc_out
 

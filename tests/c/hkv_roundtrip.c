@@ -196,13 +196,18 @@ int main(int argc, char** argv) {
     return 4;
   }
   void* d_ws = device_filled((size_t)ws_bytes, 0x5A);
+  hipEvent_t records_ready;
+  CHECK_HIP(hipEventCreateWithFlags(&records_ready, hipEventDisableTiming));
   if (fmt == HKV_FP8_E4M3)
     CHECK_HKV(hkv_quant_fp8_crc(&shape, &src, src_dtype, d_put, &rec2, d_crc2, d_ws, ws_bytes,
-                                stream));
+                                stream, records_ready));
   else
     CHECK_HKV(hkv_quant_int4_crc(&shape, &src, src_dtype, d_put, &rec2, d_crc2, d_ws, ws_bytes,
-                                 stream));
+                                 stream, records_ready));
   CHECK_HIP(hipStreamSynchronize(stream));
+  /* recorded by the call, so complete once the stream is */
+  CHECK_HIP(hipEventQuery(records_ready));
+  CHECK_HIP(hipEventDestroy(records_ready));
 
   save_records(dir, "records.bin", d_rec, L, nb, stride, rb);
   save_records(dir, "records_fused.bin", d_rec2, L, nb, stride, rb);

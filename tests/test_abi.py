@@ -352,7 +352,7 @@ def test_fused_put_crc_rejects_bad_arguments():
                                              1) == 0
     call = lambda crc=FAKE, ws=FAKE + 4096, wsb=need, sh=s: lib.hkv_quant_fp8_crc(
         ctypes.byref(sh), ctypes.byref(p), 0, ctypes.c_void_p(FAKE), ctypes.byref(r),
-        ctypes.c_void_p(crc), ctypes.c_void_p(ws), wsb, None)
+        ctypes.c_void_p(crc), ctypes.c_void_p(ws), wsb, None, None)
     assert call(crc=0) == H.ERR_INVALID_ARG
     assert call(ws=0) == H.ERR_INVALID_ARG
     assert call(wsb=need - 1) == H.ERR_INVALID_ARG

@@ -273,6 +273,47 @@ def test_fused_put_crc_other_sources(fmt, src_dtype):
             assert (got[:, b] == 0x1234567).all(), f"skipped block {b} CRC was written"
 
 
+@pytest.mark.parametrize("fmt,shape", [("fp8", (64, 8, 4, 96)), ("int4", (64, 8, 4, 96)),
+                                       ("fp8", (37, 9, 2, 24))])
+def test_fused_put_crc_records_ready(fmt, shape):
+    """records_ready: a second stream that waits on the event the fused call
+    records after its put (before the CRC merge; on the put-then-CRC path
+    before the CRC kernel) sees the complete records, and the CRCs are right
+    once the call's stream is done."""
+    tb, H, L, P = shape
+    print(f"[small] records_ready {fmt} {shape}", flush=True)
+    rng = np.random.default_rng(77)
+    kp = rng.standard_normal((L, P, tb, H, 128)).astype(np.float32)
+    vp = rng.standard_normal((L, P, tb, H, 128)).astype(np.float32)
+    table = rng.permutation(P).astype(np.int32)
+    table[3] = -1
+    rec, ref, live = _put_both(kp, vp, table, fmt, "bf16")
+    kt = torch.from_numpy(kp).to(DEV, torch.bfloat16)
+    vt = torch.from_numpy(vp).to(DEV, torch.bfloat16)
+    rec2 = hkv.alloc_records(L, len(table), fmt, tb, H, device=DEV)
+    rec2.fill_(0xA5)
+    tab = _dev_i32(table)
+    crc = torch.full((L, len(table)), 0x1234567, dtype=torch.int32, device=DEV)
+    put_stream, side = torch.cuda.Stream(), torch.cuda.Stream()
+    ready = torch.cuda.Event()
+    snap = torch.empty_like(rec2)
+    torch.cuda.synchronize()
+    hkv.quant_crc(fmt, kt, vt, tab, rec2, crc_out=crc, stream=put_stream, records_ready=ready)
+    side.wait_event(ready)
+    with torch.cuda.stream(side):
+        snap.copy_(rec2)
+    torch.cuda.synchronize()
+    assert torch.equal(snap, rec), "a stream waiting on records_ready saw incomplete records"
+    assert torch.equal(rec2, rec)
+    got = crc_u32(crc)
+    want = O.crc32_records(ref)
+    for b in range(len(table)):
+        if live[b]:
+            assert np.array_equal(got[:, b], want[:, b]), f"block {b} CRC"
+        else:
+            assert (got[:, b] == 0x1234567).all(), f"skipped block {b} CRC was written"
+
+
 def test_binding_refuses_short_records():
     """A records tensor with too few bytes per block for the call's format
     (an INT4-sized buffer given to the FP8 put and fetch, a record-sized

@@ -262,16 +262,13 @@ def main():
 
     # per-token deltas (the same +8192 for every token), 80 launches, timed once
     dm_tok = dm.view(nb, 1).expand(nb, tb).contiguous()
-    ev_t = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-    for rep in range(2):
-        ev_t[0].record(side)
+
+    def fetch_tokens_all():
         for l in range(L):
             hkv.fetch_dequant_rope_shift_tokens(rec_l[l], "fp8", ftab, dm_tok, w.rope_base,
                                                 w.pairs, ok_l[l], ov_l[l], visit_order=order,
                                                 stream=side)
-        ev_t[1].record(side)
-        side.synchronize()
-    tok_ms = ev_t[0].elapsed_time(ev_t[1])
+    tok_ms = gpu_ms(side, fetch_tokens_all, 2)
 
     # the 80 per-layer fetch launches captured once in a HIP graph and replayed
     graph = torch.cuda.CUDAGraph()
@@ -281,16 +278,7 @@ def main():
             hkv.fetch_dequant_rope_shift(rec_l[l], "fp8", ftab, dm, w.rope_base, w.pairs,
                                          ok_l[l], ov_l[l], visit_order=order)
     torch.cuda.synchronize()
-    ev_g = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-    cur = torch.cuda.current_stream(dev)
-    graph_ms = []
-    for rep in range(4):
-        ev_g[0].record(cur)
-        graph.replay()
-        ev_g[1].record(cur)
-        cur.synchronize()
-        if rep:
-            graph_ms.append(ev_g[0].elapsed_time(ev_g[1]))
+    graph_ms = gpu_ms(torch.cuda.current_stream(dev), graph.replay, 3)
     del graph
 
     if a.overlap:
@@ -391,8 +379,8 @@ def main():
             "note": "hkv_fetch_dequant_rope_shift_tokens, one delta per token",
         },
         "fetch_graph": {
-            "ms_80_layers": round(float(np.mean(graph_ms)), 4),
-            "gbps": round(fetch_bytes / (float(np.mean(graph_ms)) * 1e-3) / 1e9, 1),
+            "ms_80_layers": round(graph_ms, 4),
+            "gbps": round(fetch_bytes / (graph_ms * 1e-3) / 1e9, 1),
             "note": "the same 80 per-layer launches captured once in a HIP graph, replayed",
         },
         "put_crc": {"mean_ms": round(float(np.mean(put_crc_ms)), 4),
@@ -410,6 +398,23 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
+
+
+def gpu_ms(stream, fn, reps):
+    """Mean GPU time per call of fn() over `reps` back-to-back calls on
+    `stream`, from HIP events.  One untimed call goes first, so the GPU is
+    busy while the timed calls are enqueued and the host's own time per call
+    stays outside the events (every leg timed this way runs far longer on
+    the GPU than its call takes on the host)."""
+    import torch
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    fn()
+    ev[0].record(stream)
+    for _ in range(reps):
+        fn()
+    ev[1].record(stream)
+    stream.synchronize()
+    return ev[0].elapsed_time(ev[1]) / reps
 
 
 def stream_ceiling(dev, hkv, fetch_launch_bytes, fetch_gbps, nbuf=16, reps=64):
@@ -477,25 +482,13 @@ def separate_put_crc(dev, hkv, L, nb, tb, H, src_k, src_v, put_tab, records, crc
     """The put (hkv_quant_fp8) and the CRC (hkv_crc32_blocks) as two passes over
     the same cache, each timed with HIP events on the current stream; their
     CRCs must equal the fused pass's from the step."""
-    import numpy as np
     import torch
     s = torch.cuda.current_stream(dev)
     crc2 = torch.empty_like(crc)
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
-    put_ms, crc_ms = [], []
-    for rep in range(reps + 1):
-        ev[0].record(s)
-        hkv.quant_fp8(src_k, src_v, put_tab, records, stream=s)
-        ev[1].record(s)
-        hkv.crc32_blocks(records, "fp8", tb, H, out=crc2, stream=s)
-        ev[2].record(s)
-        s.synchronize()
-        if rep:
-            put_ms.append(ev[0].elapsed_time(ev[1]))
-            crc_ms.append(ev[1].elapsed_time(ev[2]))
+    pm = gpu_ms(s, lambda: hkv.quant_fp8(src_k, src_v, put_tab, records, stream=s), reps)
+    cm = gpu_ms(s, lambda: hkv.crc32_blocks(records, "fp8", tb, H, out=crc2, stream=s), reps)
     if not torch.equal(crc, crc2):
         raise RuntimeError("the CRC kernel disagrees with the fused put + CRC")
-    pm, cm = float(np.mean(put_ms)), float(np.mean(crc_ms))
     return {"put": {"mean_ms": round(pm, 4), "gbps": round(put_bytes / (pm * 1e-3) / 1e9, 1),
                     "note": "hkv_quant_fp8 alone"},
             "crc32": {"mean_ms": round(cm, 4), "gbps": round(crc_bytes / (cm * 1e-3) / 1e9, 1),
@@ -507,7 +500,6 @@ def other_workloads(dev, hkv, W, reps=5):
     (FP8, fp16 pages, random per-block deltas) and INT4 disk-tier (fp16 with
     outlier channels) caches, all layers in one call per operation.  Outside
     the step; HIP events."""
-    import numpy as np
     import torch
     res = {}
     for w, fmt in ((W.QWEN3_8B, "fp8"), (W.INT4_L3, "int4")):
@@ -531,39 +523,23 @@ def other_workloads(dev, hkv, W, reps=5):
         out_v = torch.empty_like(src_k)
         put = hkv.quant_fp8 if fmt == "fp8" else hkv.quant_int4
         s = torch.cuda.current_stream(dev)
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
-        put_ms, fetch_ms = [], []
-        for rep in range(reps + 1):
-            ev[0].record(s)
-            put(src_k, src_v, put_tab, rec, stream=s)
-            ev[1].record(s)
-            hkv.fetch_dequant_rope_shift(rec, fmt, ftab, dm, w.rope_base, w.pairs, out_k, out_v,
-                                         visit_order=order, stream=s)
-            ev[2].record(s)
-            s.synchronize()
-            if rep:
-                put_ms.append(ev[0].elapsed_time(ev[1]))
-                fetch_ms.append(ev[1].elapsed_time(ev[2]))
+        pms = gpu_ms(s, lambda: put(src_k, src_v, put_tab, rec, stream=s), reps)
+        fms = gpu_ms(s, lambda: hkv.fetch_dequant_rope_shift(
+            rec, fmt, ftab, dm, w.rope_base, w.pairs, out_k, out_v, visit_order=order,
+            stream=s), reps)
         # the put with the CRC-32 of every record in one pass (the disk tier
         # writes its records with their CRCs)
         crc = torch.empty((L, nb), dtype=torch.int32, device=dev)
         ws = torch.empty(max(16, hkv.quant_crc_workspace_bytes(fmt, L, nb, tb, H)),
                          dtype=torch.uint8, device=dev)
-        put_crc_ms = []
-        for rep in range(reps + 1):
-            ev[0].record(s)
-            hkv.quant_crc(fmt, src_k, src_v, put_tab, rec, crc_out=crc, workspace=ws, stream=s)
-            ev[1].record(s)
-            s.synchronize()
-            if rep:
-                put_crc_ms.append(ev[0].elapsed_time(ev[1]))
+        pcms = gpu_ms(s, lambda: hkv.quant_crc(fmt, src_k, src_v, put_tab, rec, crc_out=crc,
+                                               workspace=ws, stream=s), reps)
         del crc, ws
         cb = 128 if fmt == "fp8" else 64
         vecs = 2 * L * w.n_tokens * H
         es = src_k.element_size()
         fetch_bytes = vecs * (cb + 2 + 128 * es) + L * nb * 8
         put_bytes = vecs * (128 * es + cb + 2) + L * nb * 4
-        fms, pms = float(np.mean(fetch_ms)), float(np.mean(put_ms))
         res[w.name] = {
             "format": fmt,
             "fetch_ms": round(fms, 4),
@@ -572,9 +548,8 @@ def other_workloads(dev, hkv, W, reps=5):
             "fetch_tokens_per_s": round(w.n_tokens / (fms * 1e-3), 0),
             "put_ms": round(pms, 4),
             "put_gbps": round(put_bytes / (pms * 1e-3) / 1e9, 1),
-            "put_crc_ms": round(float(np.mean(put_crc_ms)), 4),
-            "put_crc_gbps_put_bytes": round(put_bytes / (float(np.mean(put_crc_ms)) * 1e-3) / 1e9,
-                                            1),
+            "put_crc_ms": round(pcms, 4),
+            "put_crc_gbps_put_bytes": round(put_bytes / (pcms * 1e-3) / 1e9, 1),
         }
         del src_k, src_v, rec, out_k, out_v
         torch.cuda.empty_cache()
@@ -587,7 +562,6 @@ def tp8_shard(dev, hkv, W, reps=5):
     (17.0 MB read and 33.6 MB written per layer fetch).  Put and CRC in one
     pass, then the 80 per-layer fetches on one stream, launched eagerly and
     replayed from a HIP graph.  Outside the step; HIP events."""
-    import numpy as np
     import torch
     w = W.LLAMA3_70B_TP8
     L, nb, tb, H = w.n_layers, w.n_blocks, w.block_tokens, w.n_kv_heads
@@ -620,18 +594,9 @@ def tp8_shard(dev, hkv, W, reps=5):
             hkv.fetch_dequant_rope_shift(rec_l[l], "fp8", ftab, dm, w.rope_base, w.pairs,
                                          ok_l[l], ov_l[l], visit_order=order, stream=s)
 
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
-    put_ms, fetch_ms = [], []
-    for rep in range(reps + 1):
-        ev[0].record(s)
-        hkv.quant_crc("fp8", src_k, src_v, put_tab, rec, crc_out=crc, workspace=ws, stream=s)
-        ev[1].record(s)
-        fetch_all()
-        ev[2].record(s)
-        s.synchronize()
-        if rep:
-            put_ms.append(ev[0].elapsed_time(ev[1]))
-            fetch_ms.append(ev[1].elapsed_time(ev[2]))
+    pms = gpu_ms(s, lambda: hkv.quant_crc("fp8", src_k, src_v, put_tab, rec, crc_out=crc,
+                                          workspace=ws, stream=s), reps)
+    fms = gpu_ms(s, fetch_all, reps)
     graph = torch.cuda.CUDAGraph()
     torch.cuda.synchronize()
     with torch.cuda.graph(graph):
@@ -639,32 +604,17 @@ def tp8_shard(dev, hkv, W, reps=5):
             hkv.fetch_dequant_rope_shift(rec_l[l], "fp8", ftab, dm, w.rope_base, w.pairs,
                                          ok_l[l], ov_l[l], visit_order=order)
     torch.cuda.synchronize()
-    cur = torch.cuda.current_stream(dev)
-    graph_ms = []
-    for rep in range(reps + 1):
-        ev[0].record(cur)
-        graph.replay()
-        ev[1].record(cur)
-        cur.synchronize()
-        if rep:
-            graph_ms.append(ev[0].elapsed_time(ev[1]))
+    gms = gpu_ms(torch.cuda.current_stream(dev), graph.replay, reps)
     del graph
     # the same 80 layers in one call (one launch): the kernel without the
     # per-launch ramp and drain
-    one_ms = []
-    for rep in range(reps + 1):
-        ev[0].record(s)
-        hkv.fetch_dequant_rope_shift(rec, "fp8", ftab, dm, w.rope_base, w.pairs, out_k, out_v,
-                                     visit_order=order, stream=s)
-        ev[1].record(s)
-        s.synchronize()
-        if rep:
-            one_ms.append(ev[0].elapsed_time(ev[1]))
+    oms = gpu_ms(s, lambda: hkv.fetch_dequant_rope_shift(
+        rec, "fp8", ftab, dm, w.rope_base, w.pairs, out_k, out_v, visit_order=order,
+        stream=s), reps)
     vecs_layer = 2 * w.n_tokens * H
     launch_bytes = vecs_layer * (130 + 256) + nb * 8
     put_bytes = L * (vecs_layer * (256 + 130) + nb * 4)
     crc_bytes = L * nb * (hkv.record_bytes("fp8", tb, H) + 4)
-    fms, gms, pms, oms = (float(np.mean(x)) for x in (fetch_ms, graph_ms, put_ms, one_ms))
     res = {
         "workload": "Llama-3-70B-shaped cache, one KV head (one GPU of TP = 8): 80 layers x "
                     "65536 tokens x 1 head x d128 bf16, blocks of 64, dm=+8192",
@@ -824,7 +774,6 @@ def recompute_select(dev, hkv, W, reps=10):
     8,192 bf16): per-token layer-0 drift, then the top 15%.  Outside the
     step; timed with HIP events on the current stream.  Algorithmic bytes of
     the drift: both rows read (2 * 8192 * 2 per token) plus the fp32 drift."""
-    import numpy as np
     import torch
     w = W.DRIFT_LLAMA3_70B
     cached, fresh = W.device_hidden_states(w, dev)
@@ -832,21 +781,10 @@ def recompute_select(dev, hkv, W, reps=10):
     k = (w.n_tokens * w.percent) // 100
     sel = torch.empty(k, dtype=torch.int32, device=dev)
     s = torch.cuda.current_stream(dev)
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
-    drift_ms, sel_ms = [], []
-    for rep in range(reps + 2):
-        ev[0].record(s)
-        hkv.token_drift(cached, fresh, out=drift, stream=s)
-        ev[1].record(s)
-        hkv.select_top_tokens(drift, k, out=sel, stream=s)
-        ev[2].record(s)
-        s.synchronize()
-        if rep >= 2:
-            drift_ms.append(ev[0].elapsed_time(ev[1]))
-            sel_ms.append(ev[1].elapsed_time(ev[2]))
+    dms = gpu_ms(s, lambda: hkv.token_drift(cached, fresh, out=drift, stream=s), reps)
+    sms = gpu_ms(s, lambda: hkv.select_top_tokens(drift, k, out=sel, stream=s), reps)
     es = cached.element_size()
     drift_bytes = w.n_tokens * (2 * w.d_model * es + 4)
-    dms = float(np.mean(drift_ms))
     gbps = drift_bytes / (dms * 1e-3) / 1e9
     del cached, fresh
     torch.cuda.empty_cache()
@@ -857,7 +795,7 @@ def recompute_select(dev, hkv, W, reps=10):
         "drift_gbps": round(gbps, 1),
         "drift_frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4),
         "drift_alg_bytes": drift_bytes,
-        "select_ms": round(float(np.mean(sel_ms)), 4),
+        "select_ms": round(sms, 4),
     }
 
 

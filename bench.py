@@ -370,6 +370,10 @@ def main():
             "frac_of_peak": round(fetch_gbps / HBM_PEAK_GBPS, 4),
             "tokens_per_s": round(tokens_per_s, 0),
             "ms_80_layers": round(float(np.mean(fetch_span_ms)), 4),
+            "ms_80_layers_median": round(float(np.median(fetch_span_ms)), 4),
+            "ms_80_layers_min": round(float(np.min(fetch_span_ms)), 4),
+            "gbps_at_median": round(fetch_bytes / (float(np.median(fetch_span_ms)) * 1e-3) / 1e9,
+                                    1),
         },
         "ceiling": ceiling,
         "put_ceiling": put_ceiling,

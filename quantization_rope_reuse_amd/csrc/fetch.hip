@@ -189,8 +189,11 @@ __global__ __launch_bounds__(THREADS) void fetch_kernel(FetchParams p) {
   const int slot = bk >> 1;
   const int blk = p.order ? p.order[slot] : slot;
   if (blk < 0 || blk >= p.n_blocks) return;
-  // The page is checked only after the code loads are issued, so its load
-  // latency overlaps theirs; the records of every listed block are readable.
+  // The page entry is a scalar load (the scalar cache holds the table after
+  // the first workgroups), and the compiled kernel tests it before it issues
+  // the code loads.  A variant that kept every load ahead of one exit test
+  // (clamped block index, the loaded values used on the exit path as well)
+  // measured no faster.
   const int page = p.table[blk];
 
   constexpr int CB = FMT == kFP8 ? kHeadDim : kHeadDim / 2;

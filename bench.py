@@ -291,16 +291,13 @@ def main():
                                 put_bytes, crc_bytes)
     put_ceiling = put_stream_ceiling(dev, hkv, separate["put"]["gbps"],
                                      put_bytes / (float(np.mean(put_crc_ms)) * 1e-3) / 1e9)
+    staged = None
+    if L == w.n_layers:
+        staged = staged_overlap(dev, hkv, w, L, records, ftab, dm, order)
     frames = frames_leg(dev, hkv, W, w, L, src_k, src_v, put_tab)
     select = recompute_select(dev, hkv, W)
     others = other_workloads(dev, hkv, W)
     shard = tp8_shard(dev, hkv, W)
-    # last: its bf16 GEMMs keep the GPU at full power for about a second, and
-    # legs timed right after them ran with their compute-heavier kernels
-    # (the fused put + CRC) slower
-    staged = None
-    if L == w.n_layers:
-        staged = staged_overlap(dev, hkv, w, L, records, ftab, dm, order)
 
     if a.calibrate_copy:
         # torch.neg over 2**28 fp32 values: reads exactly 1 GiB, writes 1 GiB

@@ -699,14 +699,17 @@ def staged_overlap(dev, hkv, w, L, records, ftab, dm, order, suffix_tokens=2048,
     tf = timed(staged)
     tc = timed(lambda: compute(False))
     to = timed(lambda: (staged(), compute(True)))
-    # the pages of the overlapped run against a fetch from device memory
+    # every layer's pages of the overlapped run against a fetch from device
+    # memory (bitwise)
     ok2 = torch.empty_like(out_k[:1])
     ov2 = torch.empty_like(out_v[:1])
-    for l in (0, L - 1):
+    for l in range(L):
         hkv.fetch_dequant_rope_shift(records[l:l + 1], "fp8", ftab, dm, w.rope_base, w.pairs,
                                      ok2, ov2, visit_order=order)
-        if not (torch.equal(ok2[0], out_k[l]) and torch.equal(ov2[0], out_v[l])):
-            raise RuntimeError("the staged fetch disagrees with the fetch from device memory")
+        if not (torch.equal(ok2[0].view(torch.uint8), out_k[l].view(torch.uint8))
+                and torch.equal(ov2[0].view(torch.uint8), out_v[l].view(torch.uint8))):
+            raise RuntimeError(f"the staged fetch disagrees with the fetch from device memory "
+                               f"in layer {l}")
     extent = (nb - 1) * host_rec.stride(1) + rb
     exposed = to - tc
     res = {

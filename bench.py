@@ -388,6 +388,8 @@ def main():
             "note": "the same 80 per-layer launches captured once in a HIP graph, replayed",
         },
         "put_crc": {"mean_ms": round(float(np.mean(put_crc_ms)), 4),
+                    "median_ms": round(float(np.median(put_crc_ms)), 4),
+                    "min_ms": round(float(np.min(put_crc_ms)), 4),
                     "gbps": round((put_bytes + crc_bytes) / (float(np.mean(put_crc_ms)) * 1e-3)
                                   / 1e9, 1),
                     "note": "hkv_quant_fp8_crc: put and CRC-32 in one pass (the step's "

@@ -278,6 +278,51 @@ def test_llama3_70b_full_layerwise_side_stream():
     _whole_cache(w, "fp8", rec, src_k, src_v, put_tab, out_k, out_v, ftab, dm, crc)
 
 
+def test_llama3_70b_staged_full():
+    """The layer-wise staged fetch at full size: all 80 layers' records (from
+    the fused put) in pinned host memory, copied layer by layer into two
+    staging buffers and fetched on separate copy and fetch streams, with the
+    benchmark's table, deltas and visit order.  Every layer's pages equal,
+    byte for byte, a fetch of the same layer from device memory (whose
+    parity at this size the test above checks), so no staging buffer was
+    refilled before its fetch had read it; every layer's ready event was
+    recorded."""
+    w = W.LLAMA3_70B
+    print(f"[full] {w.name} staged", flush=True)
+    src_k, src_v, put_tab = _fill_source(w)
+    L, nb, tb, H = w.n_layers, w.n_blocks, w.block_tokens, w.n_kv_heads
+    rec = hkv.alloc_records(L, nb, "fp8", tb, H, device=DEV)
+    hkv.quant_crc("fp8", src_k, src_v, put_tab, rec)
+    del src_k, src_v
+    torch.cuda.synchronize()
+    host = torch.empty(rec.shape, dtype=torch.uint8, pin_memory=True)
+    host.copy_(rec)
+    print(f"[full] {host.numel() / 1e9:.2f} GB of records pinned", flush=True)
+    ftab = torch.from_numpy(W.fetch_table(w)).to(DEV)
+    dm = torch.from_numpy(W.delta_m(w)).to(DEV)
+    order = hkv.page_visit_order(ftab, nb)
+    out_k = canary_fill(torch.empty((L, nb, tb, H, 128), dtype=torch.bfloat16, device=DEV))
+    out_v = canary_fill(torch.empty_like(out_k))
+    staging = hkv.alloc_staging(nb, "fp8", tb, H, device=DEV)
+    copy_s, fetch_s = torch.cuda.Stream(), torch.cuda.Stream()
+    ready = [torch.cuda.Event() for _ in range(L)]
+    torch.cuda.synchronize()
+    hkv.fetch_staged(host[:, :, :hkv.record_bytes("fp8", tb, H)], "fp8", ftab, dm, w.rope_base,
+                     w.pairs, out_k, out_v, staging, visit_order=order, copy_stream=copy_s,
+                     fetch_stream=fetch_s, layer_ready=ready)
+    fetch_s.synchronize()
+    assert all(e.query() for e in ready)
+    torch.cuda.synchronize()
+    ok = torch.empty_like(out_k[:1])
+    ov = torch.empty_like(out_v[:1])
+    for l in range(L):
+        hkv.fetch_dequant_rope_shift(rec[l:l + 1], "fp8", ftab, dm, w.rope_base, w.pairs, ok, ov,
+                                     visit_order=order)
+        assert torch.equal(ok[0].view(torch.uint8), out_k[l].view(torch.uint8)), f"K layer {l}"
+        assert torch.equal(ov[0].view(torch.uint8), out_v[l].view(torch.uint8)), f"V layer {l}"
+    print(f"[full] {L} staged layers equal the device-memory fetch", flush=True)
+
+
 def test_llama3_70b_per_token_deltas_full():
     """The per-token fetch at the Llama-3-70B shape in the benchmark's launch
     configuration (one layer per launch on a side stream, blocks in page

@@ -50,6 +50,10 @@
  *   the ABI.  A launch failure is reported as HKV_ERR_HIP.
  * - head_dim must be 128 (the group of one scale).
  * - Zero layers or zero blocks is a valid empty call that launches nothing.
+ * - Every view (pages, records, frames, hidden-state rows) must address no
+ *   byte offset at or beyond 2^47 from its base, counting (count - 1) *
+ *   stride over each of its dimensions plus the last element: more than a
+ *   device can address, refused with HKV_ERR_INVALID_ARG.
  * - Block tables are int32 [n_blocks]: logical block -> page.  A negative
  *   entry means "skip this block"; an entry >= num_pages is skipped as well
  *   (it is never dereferenced).  The tables given to one call must not map

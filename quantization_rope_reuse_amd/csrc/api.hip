@@ -30,6 +30,8 @@ int64_t code_bytes(int32_t fmt) { return fmt == HKV_FP8_E4M3 ? 128 : 64; }
 
 bool valid_format(int32_t fmt) { return fmt == HKV_FP8_E4M3 || fmt == HKV_INT4; }
 
+using hkv::span_ok;
+
 // Shape checks common to every call; fills the launch geometry.
 int check_shape(const hkv_shape* s, Geometry* g) {
   if (!s) return HKV_ERR_INVALID_ARG;
@@ -52,7 +54,7 @@ int check_shape(const hkv_shape* s, Geometry* g) {
   return HKV_OK;
 }
 
-int check_pages(const hkv_pages* p, int32_t dtype, PageView* v) {
+int check_pages(const hkv_pages* p, int32_t dtype, const hkv_shape* s, PageView* v) {
   if (!p) return HKV_ERR_INVALID_ARG;
   const int es = elem_size(dtype);
   if (es == 0) return HKV_ERR_INVALID_ARG;
@@ -70,6 +72,10 @@ int check_pages(const hkv_pages* p, int32_t dtype, PageView* v) {
   v->token = p->token_stride * es;
   v->head = p->head_stride * es;
   v->num_pages = p->num_pages;
+  if (!span_ok({{s->n_layers, v->layer}, {p->num_pages, v->page}, {s->block_tokens, v->token},
+                {s->n_kv_heads, v->head}},
+               int64_t{HKV_HEAD_DIM} * es))
+    return HKV_ERR_INVALID_ARG;
   return HKV_OK;
 }
 
@@ -82,6 +88,8 @@ int check_records(const hkv_records* r, int32_t fmt, const hkv_shape* s, RecordV
   if (rb < 0) return HKV_ERR_INVALID_ARG;
   if (s->n_blocks > 1 && r->block_stride_bytes < rb) return HKV_ERR_INVALID_ARG;
   if (s->n_layers > 1 && r->layer_stride_bytes < rb) return HKV_ERR_INVALID_ARG;
+  if (!span_ok({{s->n_layers, r->layer_stride_bytes}, {s->n_blocks, r->block_stride_bytes}}, rb))
+    return HKV_ERR_INVALID_ARG;
   v->base = static_cast<uint8_t*>(r->base);
   v->layer = r->layer_stride_bytes;
   v->block = r->block_stride_bytes;
@@ -111,6 +119,10 @@ int check_frames(const hkv_shape* shape, int32_t fmt, const hkv_records* frames,
   if (shape->n_blocks > 1 && frames->block_stride_bytes < fb) return HKV_ERR_INVALID_ARG;
   if (shape->n_layers > 1 && frames->layer_stride_bytes < fb) return HKV_ERR_INVALID_ARG;
   if (*rb > (int64_t{1} << 30)) return HKV_ERR_UNSUPPORTED;
+  if (!span_ok({{shape->n_layers, frames->layer_stride_bytes},
+                {shape->n_blocks, frames->block_stride_bytes}},
+               fb))
+    return HKV_ERR_INVALID_ARG;
   v->base = static_cast<uint8_t*>(frames->base);
   v->layer = frames->layer_stride_bytes;
   v->block = frames->block_stride_bytes;
@@ -124,7 +136,7 @@ int quant_common(int32_t fmt, const hkv_shape* shape, const hkv_pages* src, int3
   RecordView rv;
   int st;
   if ((st = check_shape(shape, &g)) != HKV_OK) return st;
-  if ((st = check_pages(src, src_dtype, &pv)) != HKV_OK) return st;
+  if ((st = check_pages(src, src_dtype, shape, &pv)) != HKV_OK) return st;
   if ((st = check_records(dst, fmt, shape, &rv)) != HKV_OK) return st;
   if (!block_table && g.n_blocks > 0) return HKV_ERR_INVALID_ARG;
   if (g.n_layers == 0 || g.n_blocks == 0) return HKV_OK;
@@ -143,7 +155,7 @@ int quant_crc_check(int32_t fmt, const hkv_shape* shape, const hkv_pages* src,
                     int64_t* rb, int64_t* need) {
   int st;
   if ((st = check_shape(shape, g)) != HKV_OK) return st;
-  if ((st = check_pages(src, src_dtype, pv)) != HKV_OK) return st;
+  if ((st = check_pages(src, src_dtype, shape, pv)) != HKV_OK) return st;
   if ((st = check_records(dst, fmt, shape, rv)) != HKV_OK) return st;
   if (!block_table && g->n_blocks > 0) return HKV_ERR_INVALID_ARG;
   if (!crc_out && g->n_layers > 0 && g->n_blocks > 0) return HKV_ERR_INVALID_ARG;
@@ -212,6 +224,18 @@ int fetch_common(const hkv_shape* shape, int32_t fmt, const hkv_records* src,
 
 namespace hkv {
 
+bool span_ok(std::initializer_list<Extent> dims, int64_t tail) {
+  if (tail < 0 || tail > kMaxSpan) return false;
+  int64_t total = tail;
+  for (const Extent& d : dims) {
+    if (d.count <= 1 || d.stride == 0) continue;
+    const int64_t n = d.count - 1;
+    if (d.stride < 0 || d.stride > (kMaxSpan - total) / n) return false;
+    total += n * d.stride;
+  }
+  return true;
+}
+
 int fetch_check(const hkv_shape* shape, int32_t fmt, const hkv_records* src,
                 const int32_t* block_table, const int32_t* delta_m, double rope_base,
                 int32_t pairs, const hkv_pages* dst, int32_t dst_dtype, FetchViews* f) {
@@ -219,7 +243,7 @@ int fetch_check(const hkv_shape* shape, int32_t fmt, const hkv_records* src,
   if (!valid_format(fmt)) return HKV_ERR_INVALID_ARG;
   if ((st = check_shape(shape, &f->g)) != HKV_OK) return st;
   if ((st = check_records(src, fmt, shape, &f->rv)) != HKV_OK) return st;
-  if ((st = check_pages(dst, dst_dtype, &f->pv)) != HKV_OK) return st;
+  if ((st = check_pages(dst, dst_dtype, shape, &f->pv)) != HKV_OK) return st;
   if (pairs != HKV_ROPE_INTERLEAVED && pairs != HKV_ROPE_HALF_SPLIT) return HKV_ERR_INVALID_ARG;
   if (!(rope_base > 0.0) || !isfinite(rope_base)) return HKV_ERR_INVALID_ARG;
   if ((!block_table || !delta_m) && f->g.n_blocks > 0) return HKV_ERR_INVALID_ARG;
@@ -387,6 +411,7 @@ int hkv_token_drift(const void* h_cached, const void* h_fresh, int32_t n_tokens,
   if ((reinterpret_cast<uintptr_t>(drift_out) & 3u) != 0) return HKV_ERR_INVALID_ARG;
   if (row_stride > INT64_MAX / 8 || (row_stride * es) % 16 != 0) return HKV_ERR_INVALID_ARG;
   if (n_tokens > 1 && row_stride < d_model) return HKV_ERR_INVALID_ARG;
+  if (!span_ok({{n_tokens, row_stride * es}}, int64_t{d_model} * es)) return HKV_ERR_INVALID_ARG;
   return to_status(hkv::launch_drift(dtype, h_cached, h_fresh, n_tokens, d_model,
                                      row_stride * es, drift_out, stream));
 }

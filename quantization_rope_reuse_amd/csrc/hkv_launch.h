@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <initializer_list>
+
 #include "hkv.h"
 
 namespace hkv {
@@ -56,6 +58,16 @@ hipError_t launch_crc32(const Geometry& g, int64_t record_bytes, const RecordVie
 hipError_t launch_quant_crc_units(int fmt, int src_dtype, const Geometry& g, const PageView& src,
                                   const int32_t* table, const RecordView& dst,
                                   int64_t record_bytes, uint32_t* partials, hipStream_t stream);
+
+// The largest byte offset a view addresses, (count_i - 1) * stride_i summed
+// plus `tail`, must stay below 2^47, beyond the device's virtual address
+// space (no valid buffer reaches it); the kernels' 64-bit offset arithmetic
+// then cannot overflow.  Strides are non-negative byte strides.
+constexpr int64_t kMaxSpan = int64_t{1} << 47;
+struct Extent {
+  int64_t count, stride;
+};
+bool span_ok(std::initializer_list<Extent> dims, int64_t tail);
 
 // Validated views of one fetch call (hkv_fetch_dequant_rope_shift's checks).
 struct FetchViews {

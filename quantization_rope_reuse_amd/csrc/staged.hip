@@ -67,6 +67,16 @@ extern "C" int hkv_fetch_staged(const hkv_shape* shape, int32_t fmt, const hkv_h
                             dst_dtype, &f);
   if (st != HKV_OK) return st;
   if (shape->n_layers > 65535) return HKV_ERR_UNSUPPORTED;
+  // the pages of every layer and the host records of every layer (the
+  // check above saw one layer)
+  const int64_t vec_bytes = int64_t{HKV_HEAD_DIM} * (dst_dtype == HKV_F32 ? 4 : 2);
+  if (!hkv::span_ok({{shape->n_layers, f.pv.layer}, {dst->num_pages, f.pv.page},
+                     {shape->block_tokens, f.pv.token}, {shape->n_kv_heads, f.pv.head}},
+                    vec_bytes) ||
+      !hkv::span_ok({{shape->n_layers, src->layer_stride_bytes},
+                     {shape->n_blocks, src->block_stride_bytes}},
+                    rb))
+    return HKV_ERR_INVALID_ARG;
   if (shape->n_layers == 0 || shape->n_blocks == 0) return HKV_OK;
   const int64_t extent = (static_cast<int64_t>(shape->n_blocks) - 1) * src->block_stride_bytes + rb;
   if (staging_bytes < extent) return HKV_ERR_INVALID_ARG;

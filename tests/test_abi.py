@@ -497,3 +497,54 @@ def test_binding_requires_gpu_tensors():
         H.token_drift(torch.zeros((4, 64)), torch.zeros((4, 64)))
     with pytest.raises(ValueError, match="on a GPU"):
         H.select_top_tokens(torch.zeros(64), 8)
+
+
+def test_views_beyond_the_address_space_are_rejected():
+    """A view whose largest addressed byte offset reaches 2^47 (more than a
+    device can address, so no valid buffer) is refused before any launch:
+    the kernels' 64-bit offset arithmetic can then never overflow."""
+    lib = H.lib()
+    big = 1 << 47
+    s = _shape()                                   # 2 layers, 4 blocks of 16 x 8, fp32 pages
+    # pages: one layer stride of 2^47 bytes (fp32: 2^45 elements)
+    assert _quant(s, _pages(layer_stride=big // 4), 0, FAKE, _recs()) == H.ERR_INVALID_ARG
+    # the same just below the limit passes the checks (an empty call then launches nothing)
+    assert _quant(_shape(n_blocks=0), _pages(layer_stride=(big - (1 << 20)) // 4), 0, 0,
+                  _recs()) == H.OK
+    # pages: the page stride over num_pages, the token and head strides
+    assert _quant(s, _pages(page_stride=big // 8), 0, FAKE, _recs()) == H.ERR_INVALID_ARG
+    assert _quant(_shape(block_tokens=2), _pages(token_stride=big // 4), 0, FAKE,
+                  _recs(layer_stride_bytes=4 * 4160, block_stride_bytes=4160)) == \
+        H.ERR_INVALID_ARG
+    assert _quant(_shape(n_kv_heads=2, block_tokens=8), _pages(head_stride=big // 4), 0, FAKE,
+                  _recs(layer_stride_bytes=4 * 4160, block_stride_bytes=4160)) == \
+        H.ERR_INVALID_ARG
+    # records: block and layer strides
+    assert _quant(s, _pages(), 0, FAKE, _recs(block_stride_bytes=big // 2)) == H.ERR_INVALID_ARG
+    assert _quant(s, _pages(), 0, FAKE, _recs(layer_stride_bytes=big)) == H.ERR_INVALID_ARG
+    # fetch: the destination pages and the records
+    assert _fetch(s, _recs(), FAKE, FAKE, 1e4, 0, _pages(layer_stride=big // 4), 0) == \
+        H.ERR_INVALID_ARG
+    assert _fetch(s, _recs(block_stride_bytes=big // 2), FAKE, FAKE, 1e4, 0, _pages(), 0) == \
+        H.ERR_INVALID_ARG
+    # CRC over records
+    assert lib.hkv_crc32_blocks(ctypes.byref(s), 0, ctypes.byref(_recs(layer_stride_bytes=big)),
+                                ctypes.c_void_p(FAKE), None) == H.ERR_INVALID_ARG
+    # frames
+    assert lib.hkv_frame_verify(ctypes.byref(s), 0,
+                                ctypes.byref(_frames_view(block_stride_bytes=big // 2)), 0,
+                                ctypes.c_void_p(FAKE), None) == H.ERR_INVALID_ARG
+    # drift rows (bf16: 2^46 elements per row is 2^47 bytes)
+    assert _drift(stride=big // 2) == H.ERR_INVALID_ARG
+    # staged fetch: the host records and every layer's destination pages
+    rb = 33280
+
+    def staged(ls=4 * rb, pages=_pages()):
+        hr = H.HostRecords(FAKE, ls, rb)
+        return lib.hkv_fetch_staged(ctypes.byref(s), 0, ctypes.byref(hr),
+                                    ctypes.c_void_p(FAKE + (1 << 24)),
+                                    ctypes.c_void_p(FAKE + (1 << 25)), 4 * rb,
+                                    ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE), None, 1e4, 0,
+                                    ctypes.byref(pages), 0, None, None, None)
+    assert staged(ls=big) == H.ERR_INVALID_ARG
+    assert staged(pages=_pages(layer_stride=big // 4)) == H.ERR_INVALID_ARG
